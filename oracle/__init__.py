@@ -1,0 +1,224 @@
+"""Plain fp64 CPU oracle for the weighted SiTU-GLU (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of ``bench.py`` may import this package; the product path never does.  The
+arithmetic lives in ``situ_oracle.c`` (plain C, double precision, libm), which
+shares nothing with the HIP library.  This module only compiles it with gcc,
+loads it with ctypes and marshals numpy arrays.
+
+Definitions followed (see the header of ``situ_oracle.c``):
+  * Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine", section
+    "Activation": T_g = b1*tanh(G/b1)*sigmoid(G), T_u = b2*tanh(U/b2),
+    Y = T_g*T_u.
+  * NeMo AutoModel "kimi_k3.situ" page, ``_situ_fwd_core`` (result
+    situ(g)*up(u0)*w), ``_situ_bwd_core`` (analytic dG, dU and the optional
+    routing-weight reduction), ``_WeightedSiTUFunction.forward`` (gate first,
+    up second in the last axis).
+
+Row blocks can be spread over threads because every row is independent; the
+per-row arithmetic and its order are the C code's, unchanged.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "situ_oracle.c")
+_LIB = os.path.join(_HERE, "libsitu_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE double semantics)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    i64 = ctypes.c_int64
+    lib.situ_oracle_gate.restype = ctypes.c_double
+    lib.situ_oracle_gate.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.situ_oracle_gate_grad.restype = ctypes.c_double
+    lib.situ_oracle_gate_grad.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.situ_oracle_up.restype = ctypes.c_double
+    lib.situ_oracle_up.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_double]
+    lib.situ_oracle_up_grad.restype = ctypes.c_double
+    lib.situ_oracle_up_grad.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_double]
+    lib.situ_oracle_forward.restype = None
+    lib.situ_oracle_forward.argtypes = [i64, i64, _dp, _dp, i64, ctypes.c_double,
+                                        ctypes.c_int, ctypes.c_double, _dp]
+    lib.situ_oracle_backward.restype = None
+    lib.situ_oracle_backward.argtypes = [i64, i64, _dp, _dp, i64, ctypes.c_double,
+                                         ctypes.c_int, ctypes.c_double, _dp, _dp,
+                                         _dp, _dp, _dp]
+    lib.situ_oracle_bf16_bits.restype = ctypes.c_uint16
+    lib.situ_oracle_bf16_bits.argtypes = [ctypes.c_double]
+    lib.situ_oracle_bf16_bits_array.restype = None
+    lib.situ_oracle_bf16_bits_array.argtypes = [i64, _dp, ctypes.POINTER(ctypes.c_uint16)]
+    lib.situ_oracle_f32_array.restype = None
+    lib.situ_oracle_f32_array.argtypes = [i64, _dp, ctypes.POINTER(ctypes.c_float)]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle, compiling it first only if it is not built."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+        return _lib
+
+
+def _ptr(a: np.ndarray, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _as_f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _lb_args(linear_beta):
+    return (0, 0.0) if linear_beta is None else (1, float(linear_beta))
+
+
+def _blocks(rows: int, threads: int):
+    threads = max(1, min(int(threads), rows))
+    step = -(-rows // threads)
+    return [(s, min(rows, s + step)) for s in range(0, rows, step)]
+
+
+def gate(g: float, beta: float = 4.0, lib=None) -> float:
+    return (lib or load()).situ_oracle_gate(float(g), float(beta))
+
+
+def gate_grad(g: float, beta: float = 4.0, lib=None) -> float:
+    return (lib or load()).situ_oracle_gate_grad(float(g), float(beta))
+
+
+def up(u: float, linear_beta=25.0, lib=None) -> float:
+    has, b = _lb_args(linear_beta)
+    return (lib or load()).situ_oracle_up(float(u), has, b)
+
+
+def up_grad(u: float, linear_beta=25.0, lib=None) -> float:
+    has, b = _lb_args(linear_beta)
+    return (lib or load()).situ_oracle_up_grad(float(u), has, b)
+
+
+def forward(gate_up, rw, beta: float = 4.0, linear_beta=25.0, threads: int = 1,
+            lib=None) -> np.ndarray:
+    """Y[rows, I] in fp64.  gate_up: [rows, 2I]; rw: [rows] or [1]."""
+    lib = lib or load()
+    gu = _as_f64(gate_up)
+    rows, two_i = gu.shape
+    inter = two_i // 2
+    r = _as_f64(rw).reshape(-1)
+    rw_rows = r.shape[0]
+    assert rw_rows in (rows, 1), "routing weights must be per row or one scalar"
+    y = np.empty((rows, inter), dtype=np.float64)
+    has, b2 = _lb_args(linear_beta)
+
+    def run(lo, hi):
+        rr = r if rw_rows == 1 else r[lo:hi]
+        lib.situ_oracle_forward(hi - lo, inter, _ptr(gu[lo:hi]), _ptr(rr),
+                                1 if rw_rows == 1 else hi - lo, float(beta),
+                                has, b2, _ptr(y[lo:hi]))
+
+    _run_blocks(run, rows, threads)
+    return y
+
+
+def backward(gate_up, rw, grad_out, beta: float = 4.0, linear_beta=25.0,
+             want_dr: bool = True, want_scales: bool = True, threads: int = 1,
+             lib=None) -> dict:
+    """Analytic backward in fp64.
+
+    Returns a dict with ``d_gate_up`` [rows, 2I], ``dr`` ([rows], [1] or None),
+    ``dr_abs`` [rows] and ``dg_scale`` [rows, I] (None unless want_scales).
+    """
+    lib = lib or load()
+    gu = _as_f64(gate_up)
+    rows, two_i = gu.shape
+    inter = two_i // 2
+    r = _as_f64(rw).reshape(-1)
+    rw_rows = r.shape[0]
+    assert rw_rows in (rows, 1), "routing weights must be per row or one scalar"
+    go = _as_f64(grad_out)
+    assert go.shape == (rows, inter)
+    dgu = np.empty_like(gu)
+    scalar = rw_rows == 1 and rows != 1
+    dr_rows = np.zeros(rows, dtype=np.float64) if want_dr else None
+    dr_abs = np.empty(rows, dtype=np.float64)
+    dgs = np.empty((rows, inter), dtype=np.float64) if want_scales else None
+    has, b2 = _lb_args(linear_beta)
+    null = _dp()
+    # Row sums are always taken row by row (the one broadcast weight is
+    # repeated per row); for a broadcast weight they are added below in row
+    # order, which is the order the C code's own broadcast mode uses.
+    r_rows = np.ascontiguousarray(np.broadcast_to(r, (rows,)))
+
+    def run(lo, hi):
+        n = hi - lo
+        lib.situ_oracle_backward(
+            n, inter, _ptr(gu[lo:hi]), _ptr(r_rows[lo:hi]), n, float(beta),
+            has, b2, _ptr(go[lo:hi]), _ptr(dgu[lo:hi]),
+            _ptr(dr_rows[lo:hi]) if want_dr else null, _ptr(dr_abs[lo:hi]),
+            _ptr(dgs[lo:hi]) if want_scales else null)
+
+    _run_blocks(run, rows, threads)
+    dr = None
+    if want_dr:
+        if scalar:
+            total = 0.0
+            for v in dr_rows:
+                total += float(v)
+            dr = np.array([total], dtype=np.float64)
+        else:
+            dr = dr_rows
+    return {"d_gate_up": dgu, "dr": dr, "dr_abs": dr_abs, "dg_scale": dgs}
+
+
+def _run_blocks(fn, rows: int, threads: int):
+    if rows == 0:
+        return
+    blocks = _blocks(rows, threads)
+    if len(blocks) == 1:
+        fn(*blocks[0])
+        return
+    with ThreadPoolExecutor(max_workers=len(blocks)) as ex:
+        list(ex.map(lambda b: fn(*b), blocks))
+
+
+def round_bf16_bits(x, lib=None) -> np.ndarray:
+    """fp64 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    lib = lib or load()
+    a = _as_f64(x)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib.situ_oracle_bf16_bits_array(a.size, _ptr(a), _ptr(out, ctypes.c_uint16))
+    return out
+
+
+def round_f32(x, lib=None) -> np.ndarray:
+    """fp64 -> fp32, round to nearest even."""
+    lib = lib or load()
+    a = _as_f64(x)
+    out = np.empty(a.shape, dtype=np.float32)
+    lib.situ_oracle_f32_array(a.size, _ptr(a), _ptr(out, ctypes.c_float))
+    return out

@@ -1,0 +1,77 @@
+"""Readers for the hand-derived fixtures under tests/golden/."""
+from __future__ import annotations
+
+import math
+import os
+import re
+from fractions import Fraction
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+_LN = re.compile(r"^(-?[0-9/]+)\*ln\((\d+)\)(?:/(\d+))?$")
+
+
+def parse_rational(tok: str) -> Fraction:
+    return Fraction(tok)
+
+
+def parse_x(tok: str) -> float:
+    """A number, or k*ln(n) / k*ln(n)/m with rational k, as the nearest double."""
+    m = _LN.match(tok)
+    if m:
+        k = Fraction(m.group(1))
+        n = int(m.group(2))
+        d = int(m.group(3)) if m.group(3) else 1
+        return float(k) * math.log(n) / d
+    return float(Fraction(tok))
+
+
+def closed_forms():
+    rows = []
+    with open(os.path.join(GOLDEN, "closed_forms.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            kind, b1, b2, x, exp = line.split()
+            if b2 == "-":
+                beta2 = None          # not used by this kind
+            elif b2 == "none":
+                beta2 = "none"        # linear_beta None
+            else:
+                beta2 = float(b2)
+            rows.append({
+                "kind": kind,
+                "beta1": None if b1 == "-" else float(b1),
+                "beta2": beta2,
+                "x": parse_x(x),
+                "x_text": x,
+                "expected": Fraction(exp),
+            })
+    return rows
+
+
+def worked_cases():
+    cases = []
+    cur = None
+    with open(os.path.join(GOLDEN, "worked_rows.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, _, rest = line.partition(" ")
+            rest = rest.strip()
+            if key == "case":
+                cur = {"name": rest}
+                cases.append(cur)
+            elif key == "beta1":
+                cur["beta1"] = float(rest)
+            elif key == "beta2":
+                cur["beta2"] = None if rest == "none" else float(rest)
+            elif key in ("G", "U", "go"):
+                cur[key] = [[parse_x(t) for t in row.split()] for row in rest.split(";")]
+            elif key in ("r", "dr"):
+                cur[key] = [Fraction(t.strip()) for t in rest.split(";")]
+            else:  # Y, dG, dU: exact rationals per row
+                cur[key] = [[Fraction(t) for t in row.split()] for row in rest.split(";")]
+    return cases

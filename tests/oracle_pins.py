@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises
+AssertionError when the oracle disagrees with:
+  * hand-derived closed forms (tests/golden/*.txt),
+  * algebraic closed forms of the whole curve for b1 = 2 and b1 = 4 in terms
+    of exp(-G) / exp(-G/2), derived by hand below (not the oracle's
+    tanh/sigmoid/cosh expressions),
+  * Taylor series at 0 and exponential asymptotics in the tails,
+  * the SiLU limit b1 -> infinity against torch's silu,
+  * central finite differences of the oracle's own forward,
+  * the exact linearity of Y in the routing weight,
+  * bfloat16 / fp32 rounding by torch and numpy.
+The same functions run against mutated copies of the oracle
+(test_oracle_mutants.py): every planted mistake must trip at least one pin.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+from golden_io import closed_forms, worked_cases
+
+# tribonacci constant: real root of t^3 = t^2 + t + 1 (Cardano)
+_TRIB = (1.0 + (19.0 + 3.0 * math.sqrt(33.0)) ** (1.0 / 3.0)
+         + (19.0 - 3.0 * math.sqrt(33.0)) ** (1.0 / 3.0)) / 3.0
+
+
+def _close(got, want, rtol, atol=0.0, what=""):
+    got = float(got)
+    want = float(want)
+    assert math.isfinite(got), f"{what}: got {got}"
+    assert abs(got - want) <= atol + rtol * abs(want), \
+        f"{what}: got {got!r}, want {want!r} (diff {got - want:.3e})"
+
+
+# --------------------------------------------------------------------------
+# golden fixtures
+# --------------------------------------------------------------------------
+
+def pin_closed_forms(lib):
+    for row in closed_forms():
+        k, x, want = row["kind"], row["x"], float(row["expected"])
+        lb = None if row["beta2"] == "none" else row["beta2"]
+        if k == "gate":
+            got = oracle.gate(x, row["beta1"], lib=lib)
+        elif k == "gate_grad":
+            got = oracle.gate_grad(x, row["beta1"], lib=lib)
+        elif k == "up":
+            got = oracle.up(x, lb, lib=lib)
+        else:
+            got = oracle.up_grad(x, lb, lib=lib)
+        # x is the double nearest to an irrational point: allow |f'|*ulp(x)
+        _close(got, want, 1e-13, 1e-14, f"{k}(b1={row['beta1']}, b2={row['beta2']}, x={row['x_text']})")
+
+
+def pin_worked_rows(lib):
+    for c in worked_cases():
+        rows = len(c["G"])
+        gate_up = np.array([c["G"][i] + c["U"][i] for i in range(rows)], dtype=np.float64)
+        go = np.array(c["go"], dtype=np.float64)
+        r = np.array([float(v) for v in c["r"]], dtype=np.float64)
+        y = oracle.forward(gate_up, r, c["beta1"], c["beta2"], lib=lib)
+        b = oracle.backward(gate_up, r, go, c["beta1"], c["beta2"], want_dr=True, lib=lib)
+        inter = gate_up.shape[1] // 2
+        for i in range(rows):
+            for j in range(inter):
+                _close(y[i, j], c["Y"][i][j], 1e-12, 1e-13, f"{c['name']} Y[{i},{j}]")
+                _close(b["d_gate_up"][i, j], c["dG"][i][j], 1e-12, 1e-13, f"{c['name']} dG[{i},{j}]")
+                _close(b["d_gate_up"][i, inter + j], c["dU"][i][j], 1e-12, 1e-13, f"{c['name']} dU[{i},{j}]")
+        assert len(b["dr"]) == len(c["dr"]), c["name"]
+        for i, v in enumerate(c["dr"]):
+            _close(b["dr"][i], v, 1e-12, 1e-12, f"{c['name']} dr[{i}]")
+
+
+# --------------------------------------------------------------------------
+# whole-curve algebraic closed forms (derived by hand)
+# --------------------------------------------------------------------------
+#
+# b1 = 2, E = exp(-G):  tanh(G/2) = (1-E)/(1+E), sigmoid(G) = 1/(1+E), so
+#   T_g = 2(1-E)/(1+E)^2 and, with dE/dG = -E,
+#   T_g' = 2E(3-E)/(1+E)^3          (root at E = 3, i.e. G* = -ln 3).
+# b1 = 4, u = exp(-G/2):  tanh(G/4) = (1-u)/(1+u), sigmoid(G) = 1/(1+u^2), so
+#   T_g = 4(1-u)/((1+u)(1+u^2)) and, with du/dG = -u/2,
+#   T_g' = 4u(1+u+u^2-u^3)/((1+u)^2 (1+u^2)^2)
+#   (root where u^3 = u^2+u+1: u = tribonacci constant, G* = -2 ln(trib)).
+# (1-E) and (1-u) are evaluated with expm1 so that the pin keeps its own
+# relative accuracy near G = 0.
+# b2 = 25 (any b2), v = exp(-2U/b2): T_u = b2(1-v)/(1+v), T_u' = 4v/(1+v)^2.
+
+_GRID = np.concatenate([np.linspace(-60.0, 60.0, 241),
+                        [-1.21875, -1.2187557, -1.0986123, 1e-6, -1e-6, 3e-9, 0.0]])
+
+
+def _tg_b2(g):
+    e = math.exp(-g)
+    one_minus_e = -math.expm1(-g)      # 1 - E without cancellation near G = 0
+    return (2 * one_minus_e / (1 + e) ** 2, 2 * e * (3 - e) / (1 + e) ** 3,
+            2 * e * (3 + e) / (1 + e) ** 3)
+
+
+def _tg_b4(g):
+    u = math.exp(-g / 2)
+    d = (1 + u) ** 2 * (1 + u * u) ** 2
+    val = 4 * -math.expm1(-g / 2) / ((1 + u) * (1 + u * u))
+    der = 4 * u * (1 + u + u * u - u ** 3) / d
+    der_scale = 4 * u * (1 + u + u * u + u ** 3) / d  # same terms, all added
+    return val, der, der_scale
+
+
+def pin_gate_curve_b2(lib):
+    for g in _GRID:
+        val, der, scale = _tg_b2(float(g))
+        _close(oracle.gate(g, 2.0, lib=lib), val, 1e-12, 1e-300, f"T_g(b1=2, G={g})")
+        _close(oracle.gate_grad(g, 2.0, lib=lib), der, 1e-10, 1e-14 * scale, f"T_g'(b1=2, G={g})")
+
+
+def pin_gate_curve_b4(lib):
+    for g in _GRID:
+        val, der, scale = _tg_b4(float(g))
+        _close(oracle.gate(g, 4.0, lib=lib), val, 1e-12, 1e-300, f"T_g(b1=4, G={g})")
+        _close(oracle.gate_grad(g, 4.0, lib=lib), der, 1e-10, 1e-14 * scale, f"T_g'(b1=4, G={g})")
+
+
+def pin_gate_minimum(lib):
+    gs = -2.0 * math.log(_TRIB)
+    assert abs(gs - (-1.2187557268720125)) < 1e-15
+    u0 = _TRIB  # exp(-G*/2)
+    tmin = 4 * (1 - u0) / ((1 + u0) * (1 + u0 * u0))
+    _close(oracle.gate(gs, 4.0, lib=lib), tmin, 1e-14, 0, "T_g(G*)")
+    assert abs(oracle.gate_grad(gs, 4.0, lib=lib)) < 1e-15
+    assert oracle.gate_grad(gs - 1e-4, 4.0, lib=lib) < 0 < oracle.gate_grad(gs + 1e-4, 4.0, lib=lib)
+    # b1 = 2: root at -ln 3 with T_g = -1/4
+    assert abs(oracle.gate_grad(-math.log(3.0), 2.0, lib=lib)) < 1e-15
+    _close(oracle.gate(-math.log(3.0), 2.0, lib=lib), -0.25, 1e-14, 0, "T_g(b1=2, -ln3)")
+
+
+def pin_up_curve(lib):
+    for b2 in (25.0, 3.0):
+        for uval in np.concatenate([np.linspace(-80, 80, 161), [1e-7, -2.5e-4, 0.3]]):
+            v = math.exp(-2 * abs(uval) / b2)
+            want = math.copysign(b2 * (1 - v) / (1 + v), uval) if uval != 0 else 0.0
+            wantp = 4 * v / (1 + v) ** 2
+            if abs(uval) < 1e-3:   # (1-v) cancels: use the odd Taylor series instead
+                x = uval / b2
+                want = b2 * (x - x ** 3 / 3 + 2 * x ** 5 / 15)
+            _close(oracle.up(uval, b2, lib=lib), want, 1e-12, 1e-300, f"T_u(b2={b2}, U={uval})")
+            _close(oracle.up_grad(uval, b2, lib=lib), wantp, 1e-12, 1e-300, f"T_u'(b2={b2}, U={uval})")
+
+
+# --------------------------------------------------------------------------
+# series, asymptotics, limits, symmetry
+# --------------------------------------------------------------------------
+
+def pin_series_at_zero(lib):
+    # T_g = G/2 + G^2/4 - G^3/(6 b1^2) - G^4 (1/48 + 1/(12 b1^2)) + O(G^5)
+    for b1 in (4.0, 2.0, 7.5):
+        for g in (1e-2, -1e-2, 1e-3, -3e-4, 2.5e-5):
+            s = g / 2 + g * g / 4 - g ** 3 / (6 * b1 * b1) - g ** 4 * (1 / 48 + 1 / (12 * b1 * b1))
+            d = 0.5 + g / 2 - g * g / (2 * b1 * b1) - 4 * g ** 3 * (1 / 48 + 1 / (12 * b1 * b1))
+            _close(oracle.gate(g, b1, lib=lib), s, 2e-9, 0, f"series T_g(b1={b1}, G={g})")
+            _close(oracle.gate_grad(g, b1, lib=lib), d, 2e-8, 0, f"series T_g'(b1={b1}, G={g})")
+    # T_u = U - U^3/(3 b2^2) + 2U^5/(15 b2^4) - 17U^7/(315 b2^6) + O(U^9),
+    # T_u' = 1 - U^2/b2^2 + 2U^4/(3 b2^4) - 17U^6/(45 b2^6) + O(U^8)
+    for u in (1e-2, -3e-3, 0.5):
+        b2 = 25.0
+        _close(oracle.up(u, b2, lib=lib), u - u ** 3 / (3 * b2 * b2) + 2 * u ** 5 / (15 * b2 ** 4)
+               - 17 * u ** 7 / (315 * b2 ** 6), 1e-12, 0, f"series T_u({u})")
+        _close(oracle.up_grad(u, b2, lib=lib), 1 - u * u / (b2 * b2) + 2 * u ** 4 / (3 * b2 ** 4)
+               - 17 * u ** 6 / (45 * b2 ** 6),
+               1e-11, 0, f"series T_u'({u})")
+
+
+def pin_tails(lib):
+    # b1 = 4, large |G|: T_g = 4 - 8e^{-G/2} + 4e^{-G} + O(e^{-3G/2}),
+    # T_g' = 4e^{-G/2} - 4e^{-G} + O(e^{-3G/2});
+    # G -> -inf: T_g = -4e^{G}(1 - 2e^{G/2} + O(e^{G})), T_g' = -4e^{G}(1 - 3e^{G/2} + O(e^{G}))
+    for g in (30.0, 45.0, 60.0):
+        _close(4.0 - oracle.gate(g, 4.0, lib=lib), 8 * math.exp(-g / 2) - 4 * math.exp(-g),
+               3e-3, 0, f"4 - T_g({g})")
+        _close(oracle.gate_grad(g, 4.0, lib=lib), 4 * math.exp(-g / 2) - 4 * math.exp(-g),
+               1e-11, 0, f"T_g'({g})")
+        _close(oracle.gate(-g, 4.0, lib=lib), -4 * math.exp(-g) * (1 - 2 * math.exp(-g / 2)),
+               1e-11, 0, f"T_g(-{g})")
+        _close(oracle.gate_grad(-g, 4.0, lib=lib), -4 * math.exp(-g) * (1 - 3 * math.exp(-g / 2)),
+               1e-11, 0, f"T_g'(-{g})")
+    # saturation limits
+    assert oracle.gate(800.0, 4.0, lib=lib) == 4.0
+    assert oracle.gate(-800.0, 4.0, lib=lib) == 0.0
+    assert oracle.up(1e4, 25.0, lib=lib) == 25.0
+    assert oracle.up(-1e4, 25.0, lib=lib) == -25.0
+
+
+def pin_silu_limit(lib):
+    import torch
+    g = np.linspace(-30, 30, 121)
+    silu = torch.nn.functional.silu(torch.tensor(g, dtype=torch.float64)).numpy()
+    sig = torch.sigmoid(torch.tensor(g, dtype=torch.float64)).numpy()
+    dsilu = sig * (1 + g * (1 - sig))   # textbook derivative of x*sigmoid(x)
+    for i, x in enumerate(g):
+        _close(oracle.gate(x, 1e8, lib=lib), silu[i], 1e-12, 1e-300, f"SiLU limit T_g({x})")
+        _close(oracle.gate_grad(x, 1e8, lib=lib), dsilu[i], 1e-10, 1e-15, f"SiLU limit T_g'({x})")
+
+
+def pin_up_symmetry_and_bounds(lib):
+    rng = np.random.default_rng(1)
+    for b2 in (25.0, 0.7, 300.0):
+        for uval in np.concatenate([rng.normal(0, 40, 200), [0.0, 1e-30, 5e3, 1e300]]):
+            a = oracle.up(uval, b2, lib=lib)
+            assert oracle.up(-uval, b2, lib=lib) == -a, "T_u must be odd"
+            assert abs(a) <= b2, "T_u must be bounded by b2"
+            assert 0.0 <= oracle.up_grad(uval, b2, lib=lib) <= 1.0
+    # linear_beta None: identity, derivative 1, bit for bit
+    for uval in (0.1, -3.75, 1e-40, 7e30):
+        assert oracle.up(uval, None, lib=lib) == uval
+        assert oracle.up_grad(uval, None, lib=lib) == 1.0
+    # b2 -> infinity approaches the identity
+    _close(oracle.up(3.0, 1e9, lib=lib), 3.0, 1e-15, 0, "b2 -> inf")
+
+
+# --------------------------------------------------------------------------
+# gradients by finite differences of the forward
+# --------------------------------------------------------------------------
+
+def _tiny_case(seed, rows=3, inter=6):
+    rng = np.random.default_rng(seed)
+    g = rng.normal(0, 2, (rows, inter))
+    u = rng.normal(0, 3, (rows, inter))
+    special = [40.0, -40.0, -1.21875, 0.0, 1e-6, 2 * math.log(3)]
+    g[0, :len(special)] = special[:inter]
+    u[1, :3] = [35.0, -1e-6, 0.0]
+    go = rng.normal(0, 1, (rows, inter))
+    r = rng.uniform(0.1, 1.0, rows)
+    return np.concatenate([g, u], axis=1), r, go
+
+
+def _fd(f, x, h):
+    d1 = (f(x + h) - f(x - h)) / (2 * h)
+    d2 = (f(x + h / 2) - f(x - h / 2)) / h
+    return (4 * d2 - d1) / 3      # Richardson: error O(h^4)
+
+
+def pin_fd_gradients(lib):
+    for b1, b2 in ((4.0, 25.0), (2.5, None), (4.0, None), (9.0, 3.0)):
+        gu, r, go = _tiny_case(7)
+        rows, two_i = gu.shape
+        inter = two_i // 2
+        b = oracle.backward(gu, r, go, b1, b2, want_dr=True, lib=lib)
+        y0 = oracle.forward(gu, r, b1, b2, lib=lib)
+        for i in range(rows):
+            for j in range(two_i):
+                def f(x, i=i, j=j):
+                    p = gu.copy()
+                    p[i, j] = x
+                    return oracle.forward(p, r, b1, b2, lib=lib)[i, j % inter] * go[i, j % inter]
+                x0 = gu[i, j]
+                h = 1e-3 * max(1.0, abs(x0))
+                fd = _fd(f, x0, h)
+                an = b["d_gate_up"][i, j]
+                if j < inter:
+                    scale = b["dg_scale"][i, j]
+                else:
+                    scale = abs(an) + abs(y0[i, j - inter] * go[i, j - inter])
+                assert abs(fd - an) <= 1e-7 * scale + 1e-12, \
+                    f"FD b1={b1} b2={b2} [{i},{j}] x={x0}: fd={fd!r} analytic={an!r}"
+
+
+def pin_dr(lib):
+    gu, r, go = _tiny_case(11, rows=4, inter=5)
+    for b1, b2 in ((4.0, 25.0), (3.0, None)):
+        b = oracle.backward(gu, r, go, b1, b2, want_dr=True, lib=lib)
+        y = oracle.forward(gu, r, b1, b2, lib=lib)
+        for i in range(gu.shape[0]):
+            # Y is linear in r_i, so the central difference is exact up to rounding
+            def loss(ri, i=i):
+                rr = r.copy()
+                rr[i] = ri
+                return float(np.sum(oracle.forward(gu, rr, b1, b2, lib=lib)[i] * go[i]))
+            h = 0.25
+            fd = (loss(r[i] + h) - loss(r[i] - h)) / (2 * h)
+            scale = b["dr_abs"][i]
+            _close(b["dr"][i], fd, 0, 1e-12 * scale + 1e-300, f"dr FD row {i}")
+            # r_i * dr_i = sum_j go_ij * Y_ij
+            _close(r[i] * b["dr"][i], float(np.sum(go[i] * y[i])), 0, 1e-12 * scale * r[i],
+                   f"r*dr identity row {i}")
+        # one broadcast weight: dr is the sum over rows, and the C code's own
+        # broadcast mode agrees with the row-by-row path
+        rs = np.array([0.37])
+        bs = oracle.backward(gu, rs, go, b1, b2, want_dr=True, lib=lib)
+        rowsum = oracle.backward(gu, np.full(gu.shape[0], 0.37), go, b1, b2, want_dr=True, lib=lib)["dr"]
+        _close(bs["dr"][0], float(np.sum(rowsum)), 0, 1e-12 * float(np.sum(bs["dr_abs"])), "broadcast dr")
+        import ctypes
+        dp = ctypes.POINTER(ctypes.c_double)
+        dr1 = np.zeros(1)
+        dgu = np.empty_like(gu)
+        guc = np.ascontiguousarray(gu)
+        goc = np.ascontiguousarray(go)
+        lib.situ_oracle_backward(gu.shape[0], gu.shape[1] // 2, guc.ctypes.data_as(dp),
+                                 rs.ctypes.data_as(dp), 1, b1, 0 if b2 is None else 1,
+                                 0.0 if b2 is None else b2, goc.ctypes.data_as(dp),
+                                 dgu.ctypes.data_as(dp), dr1.ctypes.data_as(dp), dp(), dp())
+        assert dr1[0] == bs["dr"][0]
+        np.testing.assert_array_equal(dgu, bs["d_gate_up"])
+
+
+def pin_row_independence(lib):
+    gu, r, go = _tiny_case(3, rows=9, inter=4)
+    y = oracle.forward(gu, r, 4.0, 25.0, lib=lib)
+    y3 = oracle.forward(gu, r, 4.0, 25.0, threads=3, lib=lib)
+    np.testing.assert_array_equal(y, y3)
+    ys = oracle.forward(gu[2:5], r[2:5], 4.0, 25.0, lib=lib)
+    np.testing.assert_array_equal(ys, y[2:5])
+    b = oracle.backward(gu, r, go, 4.0, 25.0, lib=lib)
+    b4 = oracle.backward(gu, r, go, 4.0, 25.0, threads=4, lib=lib)
+    for k in ("d_gate_up", "dr", "dr_abs", "dg_scale"):
+        np.testing.assert_array_equal(b[k], b4[k])
+
+
+# --------------------------------------------------------------------------
+# rounding
+# --------------------------------------------------------------------------
+
+_BF16_CASES = [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                 # tie, even neighbour is 1.0
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie, even neighbour is above
+    (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),    # just above the tie
+    (-(1.0 + 2.0 ** -8 - 2.0 ** -40), 0xBF80), # just below the tie, negative
+    (2.0 ** -133, 0x0001),                     # smallest subnormal
+    (2.0 ** -134, 0x0000),                     # tie between 0 and 2^-133 -> 0
+    (3 * 2.0 ** -134, 0x0002),                 # tie between 1 and 2 quanta -> 2
+    (-(2.0 ** -134) * 1.0000001, 0x8001),      # above the tie, negative
+    (2.0 ** -126, 0x0080),                     # smallest normal
+    (2.0 ** -126 - 2.0 ** -134, 0x0080),       # tie between 0x7f and 0x80 quanta -> even (0x80)
+    (3.3895313892515355e38, 0x7F7F),           # largest finite
+    (255.5 * 2.0 ** 120, 0x7F80),              # halfway to 2^128: ties to even -> inf
+    (255.49 * 2.0 ** 120, 0x7F7F),
+    (-0.0, 0x8000),
+    (0.0, 0x0000),
+    (float("inf"), 0x7F80),
+    (float("-inf"), 0xFF80),
+    (1e-300, 0x0000),
+    (-1e300, 0xFF80),
+]
+
+
+def pin_bf16_rounding(lib):
+    for x, bits in _BF16_CASES:
+        got = int(oracle.round_bf16_bits([x], lib=lib)[0])
+        assert got == bits, f"bf16({x!r}) = {got:#06x}, want {bits:#06x}"
+    nan = int(oracle.round_bf16_bits([float("nan")], lib=lib)[0])
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0
+    # agreement with torch's own float32 -> bfloat16 rounding on fp32 values
+    import torch
+    rng = np.random.default_rng(5)
+    f = np.concatenate([
+        rng.normal(0, 1, 20000), rng.normal(0, 1e-38, 2000), rng.normal(0, 1e30, 2000),
+        np.ldexp(rng.integers(1, 2 ** 24, 4000).astype(np.float64), -149),
+    ]).astype(np.float32)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16_bits(f.astype(np.float64), lib=lib)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches vs torch, first x={f[bad[0]]!r}"
+
+
+def pin_f32_rounding(lib):
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.normal(0, 1, 5000), rng.normal(0, 1e-40, 500), rng.normal(0, 1e38, 500)])
+    np.testing.assert_array_equal(oracle.round_f32(x, lib=lib), x.astype(np.float32))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

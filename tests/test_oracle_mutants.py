@@ -1,0 +1,87 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant is a copy of oracle/situ_oracle.c with one plausible slip (a
+dropped term, a wrong sign, a swapped operand or index, the wrong rounding),
+compiled with gcc into a temporary directory.  The mistakes are planted in the
+CPU oracle only; no GPU code is involved.  A mutant that passes every pin
+would mean the pins cannot see that kind of error.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "situ_oracle.c")
+
+MUTANTS = {
+    "sech2_as_one_minus_tanh2": (
+        "    double c = cosh(x);\n    return 1.0 / (c * c);",
+        "    double t = tanh(x);\n    return 1.0 - t * t;"),
+    "gate_grad_drops_second_term": (
+        "return s * sech2(g / beta1) + beta1 * tanh(g / beta1) * s * sm;",
+        "return s * sech2(g / beta1);"),
+    "gate_grad_wrong_sign": (
+        "return s * sech2(g / beta1) + beta1 * tanh(g / beta1) * s * sm;",
+        "return s * sech2(g / beta1) - beta1 * tanh(g / beta1) * s * sm;"),
+    "gate_grad_sigmoid_not_mirrored": (
+        "    double sm = logistic(-g);\n    return s",
+        "    double sm = logistic(g);\n    return s"),
+    "gate_grad_missing_beta": (
+        "+ beta1 * tanh(g / beta1) * s * sm;",
+        "+ tanh(g / beta1) * s * sm;"),
+    "gate_scaled_wrong_way": (
+        "return beta1 * tanh(g / beta1) * logistic(g);",
+        "return beta1 * tanh(g * beta1) * logistic(g);"),
+    "logistic_negative_branch": (
+        "    return e / (1.0 + e);", "    return 1.0 / (1.0 + e);"),
+    "up_missing_beta2": (
+        "return has_lb ? beta2 * tanh(u / beta2) : u;", "return has_lb ? tanh(u / beta2) : u;"),
+    "up_ignores_none": (
+        "return has_lb ? beta2 * tanh(u / beta2) : u;", "return beta2 * tanh(u / (beta2 + 1e-300));"),
+    "up_grad_squared_wrong": (
+        "return has_lb ? sech2(u / beta2) : 1.0;", "return has_lb ? sech2(u / beta2) / beta2 : 1.0;"),
+    "gate_up_halves_swapped": (
+        "double tg = situ_oracle_gate(gu[j], beta1);\n            double tu = situ_oracle_up(gu[inter + j], has_lb, beta2);\n            y[",
+        "double tg = situ_oracle_gate(gu[inter + j], beta1);\n            double tu = situ_oracle_up(gu[j], has_lb, beta2);\n            y["),
+    "forward_ignores_row_weight_index": (
+        "double r = rw[rw_rows == 1 ? 0 : i];\n        const double *gu = gate_up + i * 2 * inter;\n        for",
+        "double r = rw[0];\n        const double *gu = gate_up + i * 2 * inter;\n        for"),
+    "dG_without_r": ("dgu[j] = o * r * tu * tgp;", "dgu[j] = o * tu * tgp;"),
+    "dU_uses_gate_grad": ("dgu[inter + j] = o * r * tg * tup;", "dgu[inter + j] = o * r * tgp * tup;"),
+    "dG_dU_swapped": (
+        "dgu[j] = o * r * tu * tgp;\n            dgu[inter + j] = o * r * tg * tup;",
+        "dgu[inter + j] = o * r * tu * tgp;\n            dgu[j] = o * r * tg * tup;"),
+    "dr_includes_r": ("double p = o * tg * tu;", "double p = o * r * tg * tu;"),
+    "dr_uses_abs": ("acc += p;", "acc += fabs(p);"),
+    "bf16_truncates": ("double q = nearbyint(ax / quantum);", "double q = floor(ax / quantum);"),
+    "bf16_ties_away": ("double q = nearbyint(ax / quantum);", "double q = round(ax / quantum);"),
+    "bf16_no_subnormal_floor": ("    if (e < -126)\n        e = -126;", ""),
+    "bf16_one_bit_short": ("double quantum = ldexp(1.0, e - 7);", "double quantum = ldexp(1.0, e - 6);"),
+}
+
+
+def _build_mutant(name, tmp):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} not unique/found"
+    path = os.path.join(tmp, f"m_{name}.c")
+    with open(path, "w") as f:
+        f.write(text.replace(old, new))
+    return oracle.build(src=path, out=os.path.join(tmp, f"libm_{name}.so"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = oracle.load(_build_mutant(name, tmp))
+        caught = []
+        for pin in ALL_PINS:
+            try:
+                pin(lib)
+            except (AssertionError, ValueError, FloatingPointError, OverflowError) as e:
+                caught.append(pin.__name__)
+        assert caught, f"mutant {name} passed every pin"
