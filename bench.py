@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the weighted SiTU-GLU hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload routed_top8]
+
+One step is one pass of the whole path over one batch: the forward kernel and
+the backward kernel (with d_routing_weights where the workload asks for it),
+inputs already resident in HBM.  W untimed steps, then K timed steps between
+two device synchronisations.  Prints ONE JSON line:
+
+  value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
+               the method must move (every input read once, every output
+               written once) / wall time per step
+  roofline     the dominant kernel (the backward) against the MI355X HBM peak
+               (8 TB/s): algorithmic bytes per launch / its mean launch time,
+               timed with HIP events on the stream it runs on
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
+               (a reported baseline, not the target)
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SiTU-GLU fwd+bwd achieved HBM GB/s (% of MI355X peak) and rows/s, bf16"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "ffn_gated_activation_amd", "csrc", "situ_glu_kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != _kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(workload: str, sample_rows: int) -> dict:
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from ffn_gated_activation_amd.workloads import algorithmic_bytes, make_inputs
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    x = make_inputs(workload, device="cpu", seed=0, rows=sample_rows)
+    gu = x["gate_up"].double().numpy()
+    rw = x["routing_weights"].double().numpy()
+    go = x["grad_out"].double().numpy() if x["grad_out"] is not None else None
+    t0 = time.perf_counter()
+    oracle.forward(gu, rw, x["beta"], x["linear_beta"], threads=cores)
+    if go is not None:
+        oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"],
+                        want_scales=False, threads=cores)
+    dt = time.perf_counter() - t0
+    b = algorithmic_bytes(workload, rows=sample_rows)["total"]
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{workload} recipe, first {sample_rows} rows (seed 0, drawn on the host), "
+                      f"fp64 forward+backward, {dt:.2f} s wall",
+            "rows_per_s": round(sample_rows / dt, 1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="routed_top8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=32768)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the weighted SiTU-GLU path is row parallel and this build "
+              "runs on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd
+    from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(args.workload, device=dev, seed=0)
+    gu, rw, go = x["gate_up"], x["routing_weights"], x["grad_out"]
+    beta, lb, want = x["beta"], x["linear_beta"], x["want_drw"]
+    y = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
+    dgu = torch.empty_like(gu) if w.backward else None
+    drw = torch.empty_like(rw) if want else None
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        situ_glu_fwd(gu, rw, beta, lb, out=y)
+        if ev is not None:
+            ev[1].record()
+        if w.backward:
+            situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between synchronisations (wall clock) ...
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # ... and the same K steps again with HIP events around each kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if w.backward else 0.0
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ab = algorithmic_bytes(args.workload)
+    ms_per_step = wall / args.steps * 1e3
+    value = ab["total"] / (ms_per_step / 1e3) / 1e9
+    dom = "bwd" if w.backward else "fwd"
+    dom_bytes = ab[dom]
+    dom_ms = bwd_ms if w.backward else fwd_ms
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    kname = "situ_glu_bwd_kernel" if w.backward else "situ_glu_fwd_kernel"
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "rows": w.rows,
+                   "intermediate": w.inter, "beta": w.beta, "linear_beta": w.linear_beta,
+                   "passes": "fwd+bwd" + ("+d_routing_weights" if want else "") if w.backward else "fwd",
+                   "algorithmic_bytes_per_step": ab["total"]},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "rows_per_s": round(w.rows / (ms_per_step / 1e3), 1),
+        "kernels": {
+            "fwd": {"ms": round(fwd_ms, 5), "bytes": ab["fwd"],
+                    "GB/s": round(ab["fwd"] / (fwd_ms / 1e3) / 1e9, 2)},
+            "bwd": ({"ms": round(bwd_ms, 5), "bytes": ab["bwd"],
+                     "GB/s": round(ab["bwd"] / (bwd_ms / 1e3) / 1e9, 2)} if w.backward else None),
+        },
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(args.workload, dom)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _cpu_baseline(args.workload, min(args.cpu_sample_rows, w.rows))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,19 @@
+"""Weighted SiTU-GLU for AMD Instinct MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (include/situ_glu.h, built into
+libsitu_glu.so by ``python -m ffn_gated_activation_amd.build``) and a thin
+ctypes binding with the same names.  PyTorch provides device memory and
+streams only.
+"""
+from .situ_glu import (  # noqa: F401
+    situ_glu_abi_version,
+    situ_glu_bwd,
+    situ_glu_bwd_workspace_bytes,
+    situ_glu_fwd,
+    situ_glu_gate_window,
+    situ_glu_last_error,
+)
+from ._capi import SituGluError  # noqa: F401
+
+__all__ = ["situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes", "situ_glu_last_error",
+           "situ_glu_abi_version", "situ_glu_gate_window", "SituGluError"]

@@ -1,0 +1,410 @@
+// C ABI of the weighted SiTU-GLU library: argument validation, per-beta
+// constants, and dispatch to the HIP kernels.  Declarations and the contract
+// of every entry point are in include/situ_glu.h.
+#include "situ_glu.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "situ_glu_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+bool dtype_ok(int d) { return d == SITU_DTYPE_F32 || d == SITU_DTYPE_BF16; }
+int64_t dtype_bytes(int d) { return d == SITU_DTYPE_F32 ? 4 : 2; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range(const char *name, const void *p, int64_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(const Range &a, const Range &b)
+{
+    if (a.lo == a.hi || b.lo == b.hi)
+        return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Shared validation of the forward's inputs.  Fills the sizes used later.
+int check_common(const void *gate_up, int io_dtype, int64_t rows, int64_t inter,
+                 const void *rw, int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta)
+{
+    if (!dtype_ok(io_dtype))
+        return fail(SITU_ERR_INVALID_ARG, "io_dtype %d is not SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1)", io_dtype);
+    if (!dtype_ok(rw_dtype))
+        return fail(SITU_ERR_INVALID_ARG, "rw_dtype %d is not SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1)", rw_dtype);
+    if (!(std::isfinite(beta) && beta > 0.0))
+        return fail(SITU_ERR_INVALID_ARG, "beta must be finite and > 0 (got %g)", beta);
+    if (linear_beta && !(std::isfinite(*linear_beta) && *linear_beta > 0.0))
+        return fail(SITU_ERR_INVALID_ARG, "linear_beta must be finite and > 0, or NULL for None (got %g)",
+                    *linear_beta);
+    if (rows < 0 || inter < 0)
+        return fail(SITU_ERR_INVALID_ARG, "negative size (rows=%lld, intermediate=%lld)", (long long)rows,
+                    (long long)inter);
+    if (!(rw_rows == rows || rw_rows == 1))
+        return fail(SITU_ERR_INVALID_ARG,
+                    "rw_rows must equal rows (%lld) or be 1 (broadcast); got %lld", (long long)rows,
+                    (long long)rw_rows);
+    if (inter > (int64_t)0x3fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "intermediate %lld exceeds 2^30 - 1", (long long)inter);
+    if (rows > (int64_t)0x7fffffff * 4)
+        return fail(SITU_ERR_UNSUPPORTED, "rows %lld exceeds the grid limit", (long long)rows);
+    if (rows > 0 && inter > 0) {
+        if (!gate_up)
+            return fail(SITU_ERR_INVALID_ARG, "gate_up is NULL");
+        if (!rw)
+            return fail(SITU_ERR_INVALID_ARG, "routing_weights is NULL");
+        if (reinterpret_cast<uintptr_t>(gate_up) % dtype_bytes(io_dtype))
+            return fail(SITU_ERR_INVALID_ARG, "gate_up is not aligned to its element size");
+        if (reinterpret_cast<uintptr_t>(rw) % dtype_bytes(rw_dtype))
+            return fail(SITU_ERR_INVALID_ARG, "routing_weights is not aligned to its element size");
+    }
+    return SITU_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ beta constants
+namespace situ {
+namespace {
+
+// Truncated Taylor series c[k] = f^(k)(x0)/k! in long double.
+constexpr int kJ = 6;
+struct Jet {
+    long double c[kJ];
+};
+
+Jet jconst(long double v)
+{
+    Jet j{};
+    j.c[0] = v;
+    return j;
+}
+Jet jadd(const Jet &a, const Jet &b)
+{
+    Jet r;
+    for (int k = 0; k < kJ; ++k)
+        r.c[k] = a.c[k] + b.c[k];
+    return r;
+}
+Jet jsub(const Jet &a, const Jet &b)
+{
+    Jet r;
+    for (int k = 0; k < kJ; ++k)
+        r.c[k] = a.c[k] - b.c[k];
+    return r;
+}
+Jet jscale(const Jet &a, long double s)
+{
+    Jet r;
+    for (int k = 0; k < kJ; ++k)
+        r.c[k] = a.c[k] * s;
+    return r;
+}
+Jet jmul(const Jet &a, const Jet &b)
+{
+    Jet r{};
+    for (int k = 0; k < kJ; ++k)
+        for (int i = 0; i <= k; ++i)
+            r.c[k] += a.c[i] * b.c[k - i];
+    return r;
+}
+Jet jdiv(const Jet &a, const Jet &b)
+{
+    Jet q{};
+    for (int k = 0; k < kJ; ++k) {
+        long double s = a.c[k];
+        for (int i = 0; i < k; ++i)
+            s -= q.c[i] * b.c[k - i];
+        q.c[k] = s / b.c[0];
+    }
+    return q;
+}
+// exp(alpha * (x0 + d)) as a series in d
+Jet jexp_lin(long double alpha, long double x0)
+{
+    Jet r;
+    long double e = expl(alpha * x0), t = 1.0L;
+    for (int k = 0; k < kJ; ++k) {
+        r.c[k] = e * t;
+        t *= alpha / (long double)(k + 1);
+    }
+    return r;
+}
+
+// dT_g/dG for G < 0 as a series around x0 < 0, with e1 = exp(2G/b1),
+// e2 = exp(G) (so that for G < 0: sigmoid(G) = e2/(1+e2), tanh(G/b1) =
+// -(1-e1)/(1+e1), sech^2(G/b1) = 4 e1/(1+e1)^2):
+//   T_g' = e2 [4 e1 (1 + e2) - b1 (1 - e1^2)] / ((1 + e1)^2 (1 + e2)^2)
+Jet gate_grad_series(long double b1, long double x0)
+{
+    const Jet e1 = jexp_lin(2.0L / b1, x0);
+    const Jet e2 = jexp_lin(1.0L, x0);
+    const Jet one = jconst(1.0L);
+    const Jet A = jadd(one, e1), B = jadd(one, e2);
+    const Jet br = jsub(jscale(jmul(e1, B), 4.0L), jscale(jsub(one, jmul(e1, e1)), b1));
+    const Jet den = jmul(jmul(A, A), jmul(B, B));
+    return jdiv(jmul(e2, br), den);
+}
+
+// The bracket 4 e1 (1 + e2) - b1 (1 - e1^2) as a function of a = -G > 0:
+// positive at a = 0 (value 8), tends to -b1; its zero is -G*.
+long double bracket_at(long double b1, long double a)
+{
+    const long double e1 = expl(-2.0L * a / b1), e2 = expl(-a);
+    return 4.0L * e1 * (1.0L + e2) - b1 * (1.0L - e1 * e1);
+}
+
+}  // namespace
+
+GateK make_gate_consts(double beta1)
+{
+    const long double b1 = beta1;
+    GateK k{};
+    k.beta1 = (float)beta1;
+    k.k1 = (float)(-2.0L / b1 * 1.4426950408889634073599L);
+    k.y1k = (float)(2.0L / b1);
+    // root of the bracket by bisection (the bracket changes sign once)
+    long double lo = 0.0L, hi = 1.0L;
+    while (bracket_at(b1, hi) > 0.0L && hi < 1e6L)
+        hi *= 2.0L;
+    for (int it = 0; it < 200; ++it) {
+        const long double mid = 0.5L * (lo + hi);
+        if (mid == lo || mid == hi)
+            break;
+        if (bracket_at(b1, mid) > 0.0L)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const long double gstar = -0.5L * (lo + hi);
+    const float ghi = (float)gstar;
+    const Jet s = gate_grad_series(b1, (long double)ghi);
+    k.win_ghi = ghi;
+    k.c0 = (float)s.c[0];
+    k.c1 = (float)s.c[1];
+    k.c2 = (float)s.c[2];
+    k.c3 = (float)s.c[3];
+    // Half width: at most 1/64 and |G*|/4 (so that G - G*_f32 is exact), and
+    // small enough that the dropped quartic term stays below 3e-7 of the
+    // linear one: |c4/c1| hw^3 <= 3e-7 (the higher terms add less than that).
+    long double hw = 1.0L / 64.0L;
+    const long double q = fabsl(s.c[4]) > 0 ? cbrtl(3e-7L * fabsl(s.c[1] / s.c[4])) : hw;
+    if (q < hw)
+        hw = q;
+    if (fabsl(gstar) / 4.0L < hw)
+        hw = fabsl(gstar) / 4.0L;
+    k.win_hw = (float)hw;
+    return k;
+}
+
+UpK make_up_consts(double beta2)
+{
+    UpK k{};
+    k.beta2 = (float)beta2;
+    k.ku = (float)(-2.0L / (long double)beta2 * 1.4426950408889634073599L);
+    k.y2k = (float)(2.0L / (long double)beta2);
+    return k;
+}
+
+}  // namespace situ
+
+namespace {
+
+// The constants depend on beta alone; keep the last one per thread.
+const situ::GateK &gate_consts(double beta)
+{
+    thread_local double cached_beta = -1.0;
+    thread_local situ::GateK cached{};
+    if (beta != cached_beta) {
+        cached = situ::make_gate_consts(beta);
+        cached_beta = beta;
+    }
+    return cached;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+int situ_glu_abi_version(void) { return SITU_GLU_ABI_VERSION; }
+
+const char *situ_glu_last_error(void) { return g_last_error.c_str(); }
+
+size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate, int64_t rw_rows)
+{
+    if (rows < 0 || intermediate < 0 || rows > (int64_t)0x7fffffff * 4)
+        return 0;
+    if (rw_rows == 1 && rows > 1)
+        return (size_t)rows * sizeof(float);
+    return 0;
+}
+
+// Exposed for tests: the root-window constants the kernels use for a beta:
+// out[0] = G*_f32, out[1] = half width, out[2..5] = c0..c3.
+int situ_glu_gate_window(double beta, float *out)
+{
+    g_last_error.clear();
+    if (!(std::isfinite(beta) && beta > 0.0))
+        return fail(SITU_ERR_INVALID_ARG, "beta must be finite and > 0 (got %g)", beta);
+    if (!out)
+        return fail(SITU_ERR_INVALID_ARG, "out is NULL");
+    const situ::GateK k = situ::make_gate_consts(beta);
+    out[0] = k.win_ghi;
+    out[1] = k.win_hw;
+    out[2] = k.c0;
+    out[3] = k.c1;
+    out[4] = k.c2;
+    out[5] = k.c3;
+    return SITU_OK;
+}
+
+int situ_glu_fwd(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                 const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta, void *out, void *stream)
+{
+    g_last_error.clear();
+    int rc = check_common(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows,
+                          beta, linear_beta);
+    if (rc)
+        return rc;
+    if (rows == 0 || intermediate == 0)
+        return SITU_OK;
+    const int64_t es = dtype_bytes(io_dtype);
+    if (!out)
+        return fail(SITU_ERR_INVALID_ARG, "out is NULL");
+    if (reinterpret_cast<uintptr_t>(out) % es)
+        return fail(SITU_ERR_INVALID_ARG, "out is not aligned to its element size");
+    const Range r_out = range("out", out, rows * intermediate * es);
+    const Range r_in = range("gate_up", gate_up, rows * intermediate * 2 * es);
+    const Range r_rw = range("routing_weights", routing_weights, rw_rows * dtype_bytes(rw_dtype));
+    if (overlaps(r_out, r_in) || overlaps(r_out, r_rw))
+        return fail(SITU_ERR_INVALID_ARG, "out overlaps an input");
+
+    situ::FwdLaunch L{};
+    L.gate_up = gate_up;
+    L.rw = routing_weights;
+    L.rw_bf16 = rw_dtype == SITU_DTYPE_BF16;
+    L.rw_stride = rw_rows == rows ? 1 : 0;
+    L.out = out;
+    L.rows = rows;
+    L.inter = (int)intermediate;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = aligned16(gate_up) && aligned16(out) && (intermediate * es) % 16 == 0;
+    L.lb = linear_beta != nullptr;
+    L.fast = beta == 4.0;
+    L.gk = gate_consts(beta);
+    L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    const int err = situ::launch_fwd(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "forward launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
+int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                 const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta, const void *grad_out, void *d_gate_up,
+                 void *d_routing_weights, void *workspace, size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    int rc = check_common(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows,
+                          beta, linear_beta);
+    if (rc)
+        return rc;
+    const int64_t es = dtype_bytes(io_dtype);
+    const int64_t rs = dtype_bytes(rw_dtype);
+    if (d_routing_weights && reinterpret_cast<uintptr_t>(d_routing_weights) % rs)
+        return fail(SITU_ERR_INVALID_ARG, "d_routing_weights is not aligned to its element size");
+    if (rows == 0 || intermediate == 0) {
+        if (d_routing_weights && rw_rows > 0) {
+            // an empty sum: the gradient of every routing weight is zero
+            const int err = situ::launch_zero(d_routing_weights, rw_rows * rs, stream);
+            if (err)
+                return fail(SITU_ERR_DEVICE, "zero fill failed: %s", situ::device_error_string(err));
+        }
+        return SITU_OK;
+    }
+    if (!grad_out)
+        return fail(SITU_ERR_INVALID_ARG, "grad_out is NULL");
+    if (!d_gate_up)
+        return fail(SITU_ERR_INVALID_ARG, "d_gate_up is NULL");
+    if (reinterpret_cast<uintptr_t>(grad_out) % es)
+        return fail(SITU_ERR_INVALID_ARG, "grad_out is not aligned to its element size");
+    if (reinterpret_cast<uintptr_t>(d_gate_up) % es)
+        return fail(SITU_ERR_INVALID_ARG, "d_gate_up is not aligned to its element size");
+    const bool broadcast_dr = d_routing_weights && rw_rows == 1 && rows > 1;
+    const size_t need = broadcast_dr ? (size_t)rows * sizeof(float) : 0;
+    if (need) {
+        if (!workspace)
+            return fail(SITU_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
+        if (workspace_bytes < need)
+            return fail(SITU_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % sizeof(float))
+            return fail(SITU_ERR_INVALID_ARG, "workspace is not 4-byte aligned");
+    }
+    const Range in_gu = range("gate_up", gate_up, rows * intermediate * 2 * es);
+    const Range in_rw = range("routing_weights", routing_weights, rw_rows * rs);
+    const Range in_go = range("grad_out", grad_out, rows * intermediate * es);
+    const Range o_dgu = range("d_gate_up", d_gate_up, rows * intermediate * 2 * es);
+    const Range o_drw = range("d_routing_weights", d_routing_weights, d_routing_weights ? rw_rows * rs : 0);
+    const Range o_ws = range("workspace", workspace, (int64_t)need);
+    const Range ins[] = {in_gu, in_rw, in_go};
+    const Range outs[] = {o_dgu, o_drw, o_ws};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return fail(SITU_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+    if (overlaps(o_dgu, o_drw) || overlaps(o_dgu, o_ws) || overlaps(o_drw, o_ws))
+        return fail(SITU_ERR_INVALID_ARG, "output buffers overlap each other");
+
+    situ::BwdLaunch L{};
+    L.gate_up = gate_up;
+    L.rw = routing_weights;
+    L.rw_bf16 = rw_dtype == SITU_DTYPE_BF16;
+    L.rw_stride = rw_rows == rows ? 1 : 0;
+    L.grad_out = grad_out;
+    L.d_gate_up = d_gate_up;
+    L.d_rw = d_routing_weights;
+    L.row_partials = static_cast<float *>(need ? workspace : nullptr);
+    L.rows = rows;
+    L.inter = (int)intermediate;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = aligned16(gate_up) && aligned16(grad_out) && aligned16(d_gate_up) && (intermediate * es) % 16 == 0;
+    L.lb = linear_beta != nullptr;
+    L.fast = beta == 4.0;
+    L.gk = gate_consts(beta);
+    L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    const int err = situ::launch_bwd(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "backward launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal interface between the host API (situ_glu_api.cpp) and the HIP
+// kernels (situ_glu_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace situ {
+
+// Gate-branch constants for one beta (b1), computed on the host.
+//   e1 = exp(-2|G|/b1) = exp2(|G| * k1)
+//   y1 = 2|G|/b1       = |G| * y1k    (argument of 1 - e1 = 1 - exp(-y1))
+// The root window: dT_g/dG vanishes at G* < 0, where its two terms cancel.
+// Inside |G - win_ghi| <= win_hw the kernels evaluate dT_g/dG as the cubic
+// c0 + c1 d + c2 d^2 + c3 d^3 in d = G - win_ghi (the Taylor expansion at the
+// fp32 number nearest G*) instead of the cancelling difference.
+struct GateK {
+    float beta1;
+    float k1;
+    float y1k;
+    float win_ghi;
+    float win_hw;
+    float c0, c1, c2, c3;
+};
+
+// Up-branch constants (only used when linear_beta is given).
+//   v = exp(-2|U|/b2) = exp2(|U| * ku), y2 = 2|U|/b2 = |U| * y2k
+struct UpK {
+    float beta2;
+    float ku;
+    float y2k;
+};
+
+enum { IO_F32 = 0, IO_BF16 = 1 };
+
+struct FwdLaunch {
+    const void *gate_up;
+    const void *rw;
+    int rw_bf16;          // routing-weight dtype is bf16
+    int64_t rw_stride;    // 1: one weight per row, 0: one weight for all rows
+    void *out;
+    int64_t rows;
+    int inter;
+    int io;               // IO_F32 / IO_BF16
+    int vec;              // 1: 128-bit path, 0: element path
+    int lb;               // linear_beta given
+    int fast;             // beta1 == 4 specialisation
+    GateK gk;
+    UpK uk;
+};
+
+struct BwdLaunch {
+    const void *gate_up;
+    const void *rw;
+    int rw_bf16;
+    int64_t rw_stride;
+    const void *grad_out;
+    void *d_gate_up;
+    void *d_rw;           // NULL: no routing-weight gradient
+    float *row_partials;  // workspace, [rows] fp32, used when rw_stride == 0 and d_rw
+    int64_t rows;
+    int inter;
+    int io;
+    int vec;
+    int lb;
+    int fast;
+    GateK gk;
+    UpK uk;
+};
+
+// Enqueue the kernels; return the hipError_t of the launches (0 = success).
+int launch_fwd(const FwdLaunch &L, void *stream);
+int launch_bwd(const BwdLaunch &L, void *stream);
+// Zero `bytes` bytes at device pointer p with a fill kernel.
+int launch_zero(void *p, int64_t bytes, void *stream);
+const char *device_error_string(int err);
+
+// Host-side construction of GateK for a beta (root window included).
+GateK make_gate_consts(double beta1);
+UpK make_up_consts(double beta2);
+
+}  // namespace situ

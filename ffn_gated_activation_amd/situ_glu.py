@@ -1,0 +1,144 @@
+"""Python entry points of the weighted SiTU-GLU library (same names as the C ABI).
+
+These functions marshal torch tensors into the C ABI of libsitu_glu.so; every
+step of the computation runs in its HIP kernels.  There is no CPU fallback:
+without the built library or a GPU they raise.
+
+Semantics follow the NeMo AutoModel page "nemo_automodel.components.models.
+kimi_k3.situ": ``_WeightedSiTUFunction.forward(ctx, gate_up, routing_weights,
+beta, linear_beta)`` and ``backward(ctx, grad_out) -> (d_gate_up,
+d_routing_weights, None, None)``; ``_situ_rw_is_row_aligned`` for the routing
+weight layout (one weight per gate_up row, ``[..., 1]``, or a single weight
+broadcast over all rows).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _capi
+
+_DT = {torch.float32: _capi.SITU_DTYPE_F32, torch.bfloat16: _capi.SITU_DTYPE_BF16}
+
+
+def _io_dtype(t: torch.Tensor, what: str) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what} must be float32 or bfloat16, got {t.dtype}") from None
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("situ_glu runs on the GPU only: every tensor must be on a cuda device")
+
+
+def _flatten(gate_up: torch.Tensor, routing_weights: torch.Tensor):
+    if gate_up.dim() < 1 or gate_up.shape[-1] % 2:
+        raise ValueError(f"gate_up must be [..., 2*intermediate], got {tuple(gate_up.shape)}")
+    if not gate_up.is_contiguous():
+        raise ValueError("gate_up must be contiguous")
+    inter = gate_up.shape[-1] // 2
+    lead = tuple(gate_up.shape[:-1])
+    rows = 1
+    for d in lead:
+        rows *= d
+    rw = routing_weights
+    if not rw.is_contiguous():
+        raise ValueError("routing_weights must be contiguous")
+    if rw.numel() == 1:
+        rw_rows = 1
+    elif tuple(rw.shape) == lead + (1,) or (tuple(rw.shape) == lead and len(lead) > 0):
+        rw_rows = rows
+    else:
+        raise ValueError(
+            f"routing_weights of shape {tuple(rw.shape)} is neither row aligned with gate_up "
+            f"{tuple(gate_up.shape)} (expected {lead + (1,)}) nor a single broadcast weight")
+    return lead, rows, inter, rw_rows
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def situ_glu_fwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, beta: float = 4.0,
+                 linear_beta: float | None = 25.0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = r * (beta tanh(G/beta) sigmoid(G)) * (linear_beta tanh(U/linear_beta) or U).
+
+    gate_up [..., 2I] (float32 or bfloat16; G first, U second),
+    routing_weights [..., 1] row aligned, or one weight.  Returns [..., I] in
+    gate_up's dtype.
+    """
+    lib = _capi.load()
+    _check_device(gate_up, routing_weights, out)
+    io = _io_dtype(gate_up, "gate_up")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    lead, rows, inter, rw_rows = _flatten(gate_up, routing_weights)
+    if out is None:
+        out = torch.empty(lead + (inter,), dtype=gate_up.dtype, device=gate_up.device)
+    elif out.dtype != gate_up.dtype or tuple(out.shape) != lead + (inter,) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of gate_up's dtype and shape [..., I]")
+    _capi.check(lib.situ_glu_fwd(gate_up.data_ptr(), io, rows, inter, routing_weights.data_ptr(),
+                                 rwd, rw_rows, float(beta), _capi.lb_ptr(linear_beta),
+                                 out.data_ptr(), _stream()), lib)
+    return out
+
+
+def situ_glu_bwd_workspace_bytes(rows: int, intermediate: int, rw_rows: int) -> int:
+    return int(_capi.load().situ_glu_bwd_workspace_bytes(rows, intermediate, rw_rows))
+
+
+def situ_glu_bwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, grad_out: torch.Tensor,
+                 beta: float = 4.0, linear_beta: float | None = 25.0, want_drw: bool = True,
+                 d_gate_up: torch.Tensor | None = None, d_routing_weights: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """Analytic backward: returns (d_gate_up [..., 2I], d_routing_weights or None).
+
+    d_routing_weights has routing_weights' shape and dtype; with one broadcast
+    weight it is the sum over all rows.
+    """
+    lib = _capi.load()
+    _check_device(gate_up, routing_weights, grad_out, d_gate_up, d_routing_weights, workspace)
+    io = _io_dtype(gate_up, "gate_up")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    lead, rows, inter, rw_rows = _flatten(gate_up, routing_weights)
+    if grad_out.dtype != gate_up.dtype or tuple(grad_out.shape) != lead + (inter,):
+        raise ValueError(f"grad_out must be {lead + (inter,)} of dtype {gate_up.dtype}")
+    if not grad_out.is_contiguous():
+        raise ValueError("grad_out must be contiguous")
+    if d_gate_up is None:
+        d_gate_up = torch.empty_like(gate_up)
+    elif d_gate_up.dtype != gate_up.dtype or d_gate_up.shape != gate_up.shape or not d_gate_up.is_contiguous():
+        raise ValueError("d_gate_up must be a contiguous tensor like gate_up")
+    if want_drw and d_routing_weights is None:
+        d_routing_weights = torch.empty_like(routing_weights)
+    if not want_drw:
+        d_routing_weights = None
+    need = int(lib.situ_glu_bwd_workspace_bytes(rows, inter, rw_rows)) if want_drw else 0
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=gate_up.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    _capi.check(lib.situ_glu_bwd(
+        gate_up.data_ptr(), io, rows, inter, routing_weights.data_ptr(), rwd, rw_rows, float(beta),
+        _capi.lb_ptr(linear_beta), grad_out.data_ptr(), d_gate_up.data_ptr(),
+        d_routing_weights.data_ptr() if d_routing_weights is not None else None,
+        ws_ptr, ws_bytes, _stream()), lib)
+    return d_gate_up, d_routing_weights
+
+
+def situ_glu_last_error() -> str:
+    return _capi.last_error()
+
+
+def situ_glu_abi_version() -> int:
+    return int(_capi.load().situ_glu_abi_version())
+
+
+def situ_glu_gate_window(beta: float = 4.0):
+    """(G*_f32, half width, c0, c1, c2, c3) the kernels use near the root of dT_g/dG."""
+    import ctypes
+    lib = _capi.load()
+    out = (ctypes.c_float * 6)()
+    _capi.check(lib.situ_glu_gate_window(float(beta), out), lib)
+    return tuple(float(v) for v in out)

@@ -1,0 +1,144 @@
+"""Seeded synthetic inputs for the weighted SiTU-GLU workloads.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic, and both the oracle-side tests and the GPU path take their inputs
+from it.  The pages measure on no dataset: every workload is synthetic, with
+the shapes and value distributions below.
+
+Recipes (all draws from one torch.Generator seeded with `seed` on the chosen
+device, in the order gate_up -> [stress mask, magnitude, sign] -> routing
+weights -> grad_out; generated in fp32, then rounded to the io dtype with
+torch's round-to-nearest-even; "N(0, s)" means s * randn):
+
+  fp32_small    fp32 gate_up [256, 2*512] ~ N(0, 2); routing weights [256, 1]
+                ~ U(0, 1); grad_out ~ N(0, 1); beta 4, linear_beta 25;
+                forward + backward with d_routing_weights.
+  top1_fwd      bf16 gate_up [8192, 2*2048] ~ N(0, 1.5); routing weights
+                [8192, 1] = 0.2 + 0.8 U(0, 1) (stand-in for top-1 softmax
+                probabilities); beta 4, linear_beta 25; forward only.
+  dense_ffn     bf16 gate_up [16384, 2*18432] ~ N(0, 1); one routing weight
+                1.0 broadcast over all rows; linear_beta None; grad_out bf16
+                ~ N(0, 1); forward + backward, no d_routing_weights.
+  routed_top8   bf16 gate_up [65536, 2*2048] ~ N(0, 1), rows = 8192 tokens x
+                top-8 (row 8t+k); routing weights = softmax over the 8 draws
+                of N(0, 1) per token, [65536, 1] fp32; grad_out bf16 ~ N(0, 1);
+                beta 4, linear_beta 25; forward + backward with
+                d_routing_weights.
+  stress_sat    bf16 gate_up [131072, 2*2048]: N(0, 8), with 5% of entries
+                (mask U(0,1) < 0.05) replaced by sign * (30 + 30 U(0,1)),
+                sign -1 where U(0,1) < 0.5 else +1 (saturation of tanh and
+                sigmoid); routing weights [131072, 1] ~ U(0, 1); grad_out bf16
+                ~ N(0, 1); beta 4, linear_beta 25; forward + backward with
+                d_routing_weights; rows in natural order.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    rows: int
+    inter: int
+    dtype: torch.dtype
+    beta: float
+    linear_beta: float | None
+    backward: bool
+    want_drw: bool
+    broadcast_rw: bool
+    description: str
+
+
+WORKLOADS = {
+    "fp32_small": Workload("fp32_small", 256, 512, torch.float32, 4.0, 25.0, True, True, False,
+                           "fp32 gate_up [256, 2*512] ~ N(0,2), r ~ U(0,1), fwd+bwd+dr"),
+    "top1_fwd": Workload("top1_fwd", 8192, 2048, torch.bfloat16, 4.0, 25.0, False, False, False,
+                         "bf16 gate_up [8192, 2*2048] ~ N(0,1.5), r = 0.2+0.8 U(0,1), fwd only"),
+    "dense_ffn": Workload("dense_ffn", 16384, 18432, torch.bfloat16, 4.0, None, True, False, True,
+                          "bf16 dense FFN gate_up [16384, 2*18432] ~ N(0,1), r = 1.0 broadcast, "
+                          "linear_beta None, fwd+bwd"),
+    "routed_top8": Workload("routed_top8", 65536, 2048, torch.bfloat16, 4.0, 25.0, True, True, False,
+                            "bf16 routed-expert rows 8192 tokens x top-8, gate_up [65536, 2*2048] "
+                            "~ N(0,1), r = per-token softmax of 8 N(0,1) draws, fwd+bwd+dr"),
+    "stress_sat": Workload("stress_sat", 131072, 2048, torch.bfloat16, 4.0, 25.0, True, True, False,
+                           "bf16 gate_up [131072, 2*2048] N(0,8) with 5% at +-U(30,60), "
+                           "r ~ U(0,1), fwd+bwd+dr"),
+}
+ORDER = ["fp32_small", "top1_fwd", "dense_ffn", "routed_top8", "stress_sat"]
+
+
+def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
+                inter: int | None = None) -> dict:
+    """Draw one workload's inputs.  `rows` / `inter` override the shape (a
+    smaller or ragged instance of the same recipe; for routed_top8 rows must be
+    a multiple of 8)."""
+    w = WORKLOADS[name]
+    rows = w.rows if rows is None else int(rows)
+    if inter is not None:
+        from dataclasses import replace
+        w = replace(w, inter=int(inter))
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    def rand(*shape):
+        return torch.rand(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    shape = (rows, 2 * w.inter)
+    if name == "fp32_small":
+        gate_up = 2.0 * randn(*shape)
+    elif name == "top1_fwd":
+        gate_up = 1.5 * randn(*shape)
+    elif name in ("dense_ffn", "routed_top8"):
+        gate_up = randn(*shape)
+    elif name == "stress_sat":
+        gate_up = 8.0 * randn(*shape)
+        mask = rand(*shape) < 0.05
+        mag = 30.0 + 30.0 * rand(*shape)
+        sign = torch.where(rand(*shape) < 0.5, -1.0, 1.0)
+        gate_up = torch.where(mask, sign * mag, gate_up)
+        del mask, mag, sign
+    else:
+        raise KeyError(name)
+    gate_up = gate_up.to(w.dtype)
+
+    if name == "fp32_small" or name == "stress_sat":
+        rw = rand(rows, 1)
+    elif name == "top1_fwd":
+        rw = 0.2 + 0.8 * rand(rows, 1)
+    elif name == "dense_ffn":
+        rw = torch.ones(1, device=dev, dtype=torch.float32)
+    else:  # routed_top8
+        if rows % 8:
+            raise ValueError("routed_top8 rows must be a multiple of 8 (tokens x top-8)")
+        z = randn(rows // 8, 8)
+        rw = torch.softmax(z, dim=1).reshape(rows, 1).contiguous()
+
+    grad_out = randn(rows, w.inter).to(w.dtype) if w.backward else None
+    return {"workload": w, "gate_up": gate_up, "routing_weights": rw, "grad_out": grad_out,
+            "beta": w.beta, "linear_beta": w.linear_beta, "want_drw": w.want_drw}
+
+
+def algorithmic_bytes(name: str, rows: int | None = None) -> dict:
+    """Bytes the method must move: read every input once, write every output once.
+
+    forward : gate_up + routing weights + out
+    backward: gate_up + routing weights + grad_out + d_gate_up (+ d_routing_weights)
+    """
+    w = WORKLOADS[name]
+    rows = w.rows if rows is None else rows
+    s = torch.finfo(w.dtype).bits // 8
+    rw_bytes = 4 * (1 if w.broadcast_rw else rows)
+    fwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s
+    bwd = 0
+    if w.backward:
+        bwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s + rows * 2 * w.inter * s
+        if w.want_drw:
+            bwd += rw_bytes
+    return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}

@@ -1,0 +1,166 @@
+/*
+ * situ_glu.h - weighted SiTU-GLU forward and backward on AMD Instinct MI355X
+ * (gfx950), C ABI.
+ *
+ * The operation (Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer
+ * Engine", section "Activation"; NeMo AutoModel page
+ * "nemo_automodel.components.models.kimi_k3.situ", `_situ_fwd_core`):
+ *
+ *     T_g(G) = beta * tanh(G / beta) * sigmoid(G)                gate branch
+ *     T_u(U) = linear_beta * tanh(U / linear_beta)               up branch
+ *              (T_u(U) = U when linear_beta is NULL, i.e. None)
+ *     Y      = r * T_g(G) * T_u(U)
+ *
+ * with sigmoid the logistic function, G the first half and U the second half
+ * of each row of gate_up (`_WeightedSiTUFunction.forward`: "gate in the first
+ * half of the last axis, up in the second"), and r the routing weight of the
+ * row.  The Kimi K3 defaults are beta = 4 and linear_beta = 25.
+ *
+ * Layout (all buffers contiguous, row major, device memory):
+ *   gate_up          [rows, 2*intermediate]   io dtype; G = cols [0, I), U = cols [I, 2I)
+ *   out, grad_out    [rows, intermediate]     io dtype
+ *   d_gate_up        [rows, 2*intermediate]   io dtype; dG first, dU second
+ *   routing_weights  [rw_rows]                rw dtype; rw_rows == rows (one
+ *                    weight per row, the page's row-aligned [tokens, 1]) or
+ *                    rw_rows == 1 (one weight broadcast over every row)
+ *   d_routing_weights[rw_rows]                rw dtype
+ * Leading dimensions of [..., 2I] tensors are flattened into `rows` by the
+ * caller.  Any pointer alignment is accepted; 16-byte-aligned buffers with
+ * intermediate a multiple of 8 (bf16) or 4 (fp32) take the 128-bit path.
+ *
+ * Precision: inputs are widened to fp32, every intermediate is fp32 (the
+ * NeMo page's fp32 chain over low-precision saved inputs), and results are
+ * rounded once to the output dtype (round to nearest even).
+ *
+ * Ownership and streams: the caller allocates and owns every buffer.  The
+ * library never allocates, frees or keeps a pointer, and keeps no state
+ * between the forward and the backward: the caller keeps gate_up and
+ * routing_weights alive for the backward, as the autograd context does on the
+ * NeMo page.  Calls enqueue work on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronising.  Launch failures are returned;
+ * faults during execution surface at the caller's next synchronisation.
+ *
+ * Errors: every argument is validated before anything is launched; on any
+ * error nothing is written and nothing is launched, and a description is
+ * available from situ_glu_last_error() (thread local).  rows == 0 or
+ * intermediate == 0 is a valid empty call: SITU_OK, no launch.
+ *
+ * Determinism: results are bitwise reproducible for identical inputs and
+ * launch parameters, and each output row depends only on its own input row
+ * (and, for d_routing_weights with one broadcast weight, on a fixed-order sum
+ * over rows).
+ */
+#ifndef SITU_GLU_H
+#define SITU_GLU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SITU_GLU_ABI_VERSION 1
+
+/* return codes */
+#define SITU_OK 0
+#define SITU_ERR_INVALID_ARG 1  /* a rejected argument (see each entry point) */
+#define SITU_ERR_UNSUPPORTED 2  /* valid but not supported (e.g. too large) */
+#define SITU_ERR_DEVICE 3       /* the HIP runtime reported an error */
+
+/* element types */
+#define SITU_DTYPE_F32 0
+#define SITU_DTYPE_BF16 1
+
+/*
+ * Forward: out = r * T_g(G) * T_u(U).
+ * NeMo page, `_WeightedSiTUFunction.forward(ctx, gate_up, routing_weights,
+ * beta, linear_beta)` and `_situ_fwd_core`.
+ *
+ *   gate_up          device pointer, [rows, 2*intermediate] of io_dtype
+ *   io_dtype         SITU_DTYPE_F32 or SITU_DTYPE_BF16; also the dtype of out
+ *   rows, intermediate  >= 0; rows * 2 * intermediate must fit in int64
+ *   routing_weights  device pointer, [rw_rows] of rw_dtype
+ *   rw_dtype         SITU_DTYPE_F32 or SITU_DTYPE_BF16
+ *   rw_rows          rows, or 1 (one weight for every row)
+ *   beta             gate beta; finite and > 0
+ *   linear_beta      host pointer to the up-branch beta (finite, > 0), or
+ *                    NULL for None (up branch = U)
+ *   out              device pointer, [rows, intermediate] of io_dtype; must
+ *                    not overlap gate_up or routing_weights
+ *   stream           hipStream_t or NULL
+ * Returns SITU_OK, SITU_ERR_INVALID_ARG (bad dtype, beta, linear_beta,
+ * rw_rows, NULL pointer, negative size, overlapping output), or
+ * SITU_ERR_DEVICE (launch failed).
+ */
+int situ_glu_fwd(const void *gate_up, int io_dtype, int64_t rows,
+                 int64_t intermediate, const void *routing_weights,
+                 int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta, void *out, void *stream);
+
+/*
+ * Backward: recomputes the fp32 intermediates from the saved inputs and
+ * writes the analytic gradients of L = sum(grad_out * Y):
+ *     dG = grad_out * r * T_u(U) * dT_g/dG,   dU = grad_out * r * T_g(G) * dT_u/dU
+ *     dr_i = sum_j grad_out_ij * T_g(G_ij) * T_u(U_ij)        (rw_rows == rows)
+ *     dr_0 = sum_i sum_j grad_out_ij * T_g(G_ij) * T_u(U_ij)  (rw_rows == 1)
+ * with dT_g/dG = sigmoid(G) sech^2(G/beta) + beta tanh(G/beta) sigmoid(G)
+ * sigmoid(-G) and dT_u/dU = sech^2(U/linear_beta) (1 when linear_beta is
+ * NULL).  NeMo page, `_WeightedSiTUFunction.backward(ctx, grad_out) ->
+ * (d_gate_up, d_routing_weights, None, None)` and `_situ_bwd_core(g, u0, w,
+ * go, beta, linear_beta, want_drw)`.
+ *
+ *   gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype,
+ *   rw_rows, beta, linear_beta   as for situ_glu_fwd (the forward's inputs)
+ *   grad_out         device pointer, [rows, intermediate] of io_dtype
+ *   d_gate_up        device pointer, [rows, 2*intermediate] of io_dtype
+ *   d_routing_weights device pointer, [rw_rows] of rw_dtype, or NULL when the
+ *                    routing-weight gradient is not wanted (want_drw false)
+ *   workspace        device scratch of at least
+ *                    situ_glu_bwd_workspace_bytes(rows, intermediate, rw_rows)
+ *                    bytes (NULL allowed when that is 0); caller owned,
+ *                    contents on entry are ignored, clobbered on exit
+ *   workspace_bytes  size of workspace
+ *   stream           hipStream_t or NULL
+ * Outputs must not overlap any input or each other.  Returns as
+ * situ_glu_fwd; a too-small workspace is SITU_ERR_INVALID_ARG.
+ */
+int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows,
+                 int64_t intermediate, const void *routing_weights,
+                 int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta, const void *grad_out,
+                 void *d_gate_up, void *d_routing_weights, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace situ_glu_bwd needs: 0 unless one weight is broadcast
+ * over several rows (rw_rows == 1 < rows), where the fixed-order reduction of
+ * the routing-weight gradient keeps one fp32 partial per row.  Returns 0 for
+ * invalid sizes.
+ */
+size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate,
+                                    int64_t rw_rows);
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char *situ_glu_last_error(void);
+
+/* SITU_GLU_ABI_VERSION of the loaded library. */
+int situ_glu_abi_version(void);
+
+/*
+ * Diagnostic: the constants the kernels use near the root G* < 0 of dT_g/dG
+ * for a given beta (host only, no device work).  There the two terms of
+ * dT_g/dG cancel (Megatron-LM PR "Add SiTU-GLU through Transformer Engine",
+ * section "Activation": T_g has its minimum at G*), so inside
+ * |G - out[0]| <= out[1] the kernels evaluate dT_g/dG as
+ * out[2] + out[3] d + out[4] d^2 + out[5] d^3 with d = G - out[0]
+ * (out[0] = G* rounded to fp32).  out must hold 6 floats.
+ * Returns SITU_OK or SITU_ERR_INVALID_ARG (bad beta, NULL out).
+ */
+int situ_glu_gate_window(double beta, float *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SITU_GLU_H */

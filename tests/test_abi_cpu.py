@@ -1,0 +1,158 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every symbol
+include/situ_glu.h declares, and rejects invalid arguments before any device
+work (so these calls never reach the HIP runtime).  Also the host-side
+root-window constants against the oracle."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "situ_glu.h")
+
+
+@pytest.fixture(scope="module")
+def capi():
+    from ffn_gated_activation_amd import _capi
+    if not os.path.exists(_capi.LIB_PATH):
+        from ffn_gated_activation_amd.build import build_library
+        build_library()
+    return _capi
+
+
+@pytest.fixture(scope="module")
+def lib(capi):
+    return capi.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(situ_glu_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib, capi):
+    names = _declared()
+    assert set(names) == set(capi.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.situ_glu_abi_version() == 1
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "situ_glu.h"\nint main(void){return SITU_OK;}\n')
+    import subprocess
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c", str(src),
+                    "-o", str(tmp_path / "t.o")], check=True)
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, **kw):
+    a = dict(gate_up=FAKE, io=1, rows=4, inter=8, rw=FAKE + 4096, rwd=0, rw_rows=4, beta=4.0, lb=25.0,
+             out=FAKE + 8192)
+    a.update(kw)
+    lb = None if a["lb"] is None else ctypes.pointer(ctypes.c_double(a["lb"]))
+    return lib.situ_glu_fwd(a["gate_up"], a["io"], a["rows"], a["inter"], a["rw"], a["rwd"], a["rw_rows"],
+                            a["beta"], lb, a["out"], None)
+
+
+def _bwd(lib, **kw):
+    a = dict(gate_up=FAKE, io=1, rows=4, inter=8, rw=FAKE + 4096, rwd=0, rw_rows=4, beta=4.0, lb=25.0,
+             go=FAKE + 8192, dgu=FAKE + 16384, drw=FAKE + 32768, ws=None, wsb=0)
+    a.update(kw)
+    lb = None if a["lb"] is None else ctypes.pointer(ctypes.c_double(a["lb"]))
+    return lib.situ_glu_bwd(a["gate_up"], a["io"], a["rows"], a["inter"], a["rw"], a["rwd"], a["rw_rows"],
+                            a["beta"], lb, a["go"], a["dgu"], a["drw"], a["ws"], a["wsb"], None)
+
+
+BAD_FWD = [
+    dict(io=2), dict(io=-1), dict(rwd=7), dict(beta=0.0), dict(beta=-1.0), dict(beta=math.inf),
+    dict(beta=math.nan), dict(lb=0.0), dict(lb=-3.0), dict(lb=math.inf), dict(lb=math.nan),
+    dict(rows=-1), dict(inter=-2), dict(rw_rows=3), dict(rw_rows=0), dict(gate_up=None),
+    dict(rw=None), dict(out=None), dict(gate_up=FAKE + 1), dict(rw=FAKE + 4098), dict(out=FAKE + 8193),
+    dict(out=FAKE + 16), dict(out=FAKE + 4096 - 2),   # overlaps gate_up / routing weights
+]
+
+
+@pytest.mark.parametrize("kw", BAD_FWD, ids=[str(k) for k in BAD_FWD])
+def test_fwd_rejects(lib, capi, kw):
+    rc = _fwd(lib, **kw)
+    assert rc == capi.SITU_ERR_INVALID_ARG, (kw, rc)
+    assert capi.last_error(lib) != ""
+
+
+BAD_BWD = [
+    dict(io=3), dict(beta=-2.0), dict(lb=math.nan), dict(rw_rows=2), dict(go=None), dict(dgu=None),
+    dict(dgu=FAKE + 8192 + 8),                       # overlaps grad_out
+    dict(drw=FAKE + 16384 + 32),                     # overlaps d_gate_up
+    dict(drw=FAKE + 4096),                           # overlaps routing weights
+    dict(rw_rows=1),                                 # broadcast dr needs a workspace
+    dict(rw_rows=1, ws=FAKE + 65536, wsb=8),         # too small (4 rows x 4 bytes)
+    dict(rw_rows=1, ws=FAKE + 65538, wsb=64),        # misaligned workspace
+    dict(drw=FAKE + 32769),                          # misaligned d_routing_weights
+]
+
+
+@pytest.mark.parametrize("kw", BAD_BWD, ids=[str(k) for k in BAD_BWD])
+def test_bwd_rejects(lib, capi, kw):
+    rc = _bwd(lib, **kw)
+    assert rc == capi.SITU_ERR_INVALID_ARG, (kw, rc)
+    assert capi.last_error(lib) != ""
+
+
+def test_unsupported_sizes(lib, capi):
+    assert _fwd(lib, inter=1 << 30, rows=1, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+
+
+def test_workspace_bytes(lib):
+    f = lib.situ_glu_bwd_workspace_bytes
+    assert f(16384, 18432, 1) == 16384 * 4
+    assert f(65536, 2048, 65536) == 0
+    assert f(1, 8, 1) == 0
+    assert f(-1, 8, 1) == 0
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_fwd
+    with pytest.raises(ValueError):
+        situ_glu_fwd(torch.zeros(2, 8), torch.ones(2, 1))
+
+
+def test_gate_window_constants(capi, lib):
+    """The root window the kernels use agrees with the oracle: G*_f32 is the
+    float nearest the oracle's root, and the cubic matches the oracle's
+    dT_g/dG inside the window to 1e-6 relative (the polynomial itself,
+    evaluated in double)."""
+    import oracle
+    out = (ctypes.c_float * 6)()
+    for beta in (4.0, 3.0, 1.0, 0.5, 2.0, 100.0, 1e4):
+        assert lib.situ_glu_gate_window(beta, out) == 0
+        ghi, hw, c0, c1, c2, c3 = [float(v) for v in out]
+        lo, hi = -80.0, -1e-4
+        for _ in range(200):
+            mid = 0.5 * (lo + hi)
+            if oracle.gate_grad(mid, beta) < 0:
+                lo = mid
+            else:
+                hi = mid
+        root = 0.5 * (lo + hi)
+        assert abs(np.float32(root) - ghi) <= abs(np.spacing(np.float32(root))), (beta, root, ghi)
+        assert 0 < hw <= 1 / 64 and hw <= abs(ghi) / 4
+        for d in np.linspace(-hw, hw, 41):
+            g = ghi + d
+            p = c0 + d * (c1 + d * (c2 + d * c3))
+            t = oracle.gate_grad(g, beta)
+            scale = abs(c1 * (g - root)) + 1e-300
+            # coefficients are rounded to fp32: allow their rounding too
+            tol = 1e-6 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d) + abs(c3 * d ** 3))
+            assert abs(p - t) <= tol, (beta, d, p, t)
+    assert lib.situ_glu_gate_window(-1.0, out) == capi.SITU_ERR_INVALID_ARG
