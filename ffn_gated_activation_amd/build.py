@@ -44,18 +44,19 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build_library(verbose: bool = False, extra_hipcc: list[str] | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    api_o = os.path.join(BUILD, "situ_glu_api.o")
-    ker_o = os.path.join(BUILD, "situ_glu_kernels.o")
+def build_library(verbose: bool = False, extra_hipcc: list[str] | None = None, out: str = LIB,
+                  build_dir: str = BUILD) -> str:
+    os.makedirs(build_dir, exist_ok=True)
+    api_o = os.path.join(build_dir, "situ_glu_api.o")
+    ker_o = os.path.join(build_dir, "situ_glu_kernels.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
           os.path.join(CSRC, "situ_glu_api.cpp"), "-o", api_o], verbose)
     _run([_hipcc(), *HIPCC_FLAGS, *(extra_hipcc or []), "-I", INCLUDE, "-I", CSRC, "-c",
           os.path.join(CSRC, "situ_glu_kernels.hip"), "-o", ker_o], verbose)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -70,8 +71,8 @@ int check_common(const void *gate_up, int io_dtype, int64_t rows, int64_t inter,
                     (long long)rw_rows);
     if (inter > (int64_t)0x3fffffff)
         return fail(SITU_ERR_UNSUPPORTED, "intermediate %lld exceeds 2^30 - 1", (long long)inter);
-    if (rows > (int64_t)0x7fffffff * 4)
-        return fail(SITU_ERR_UNSUPPORTED, "rows %lld exceeds the grid limit", (long long)rows);
+    if (rows > (int64_t)0x7fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "rows %lld exceeds 2^31 - 1", (long long)rows);
     if (rows > 0 && inter > 0) {
         if (!gate_up)
             return fail(SITU_ERR_INVALID_ARG, "gate_up is NULL");
@@ -187,7 +188,7 @@ GateK make_gate_consts(double beta1)
     const long double b1 = beta1;
     GateK k{};
     k.beta1 = (float)beta1;
-    k.k1 = (float)(-2.0L / b1 * 1.4426950408889634073599L);
+    k.k1 = (float)(2.0L / b1 * 1.4426950408889634073599L);
     k.y1k = (float)(2.0L / b1);
     // root of the bracket by bisection (the bracket changes sign once)
     long double lo = 0.0L, hi = 1.0L;
@@ -220,6 +221,13 @@ GateK make_gate_consts(double beta1)
     if (fabsl(gstar) / 4.0L < hw)
         hw = fabsl(gstar) / 4.0L;
     k.win_hw = (float)hw;
+    // The quadratic (bf16 io, 1 ulp = 2^-8 relative) drops c3 d^3: keep
+    // |c3/c1| hw2^2 <= 1e-4, inside the cubic's window.
+    long double hw2 = hw;
+    const long double q2 = fabsl(s.c[3]) > 0 ? sqrtl(1e-4L * fabsl(s.c[1] / s.c[3])) : hw;
+    if (q2 < hw2)
+        hw2 = q2;
+    k.win_hw2 = (float)hw2;
     return k;
 }
 
@@ -227,14 +235,26 @@ UpK make_up_consts(double beta2)
 {
     UpK k{};
     k.beta2 = (float)beta2;
-    k.ku = (float)(-2.0L / (long double)beta2 * 1.4426950408889634073599L);
-    k.y2k = (float)(2.0L / (long double)beta2);
+    k.ku = (float)(2.0L / (long double)beta2 * 1.4426950408889634073599L);
     return k;
 }
 
 }  // namespace situ
 
 namespace {
+
+// Rows per workgroup of the 128-bit path when a row is one strip: 0 lets the
+// launcher choose; the environment variable SITU_GLU_ROWS_PER_BLOCK (1..16)
+// fixes it (tuning).
+int rows_per_block_override()
+{
+    static const int v = [] {
+        const char *e = std::getenv("SITU_GLU_ROWS_PER_BLOCK");
+        const int x = e ? std::atoi(e) : 0;
+        return (x >= 1 && x <= 16) ? x : 0;
+    }();
+    return v;
+}
 
 // The constants depend on beta alone; keep the last one per thread.
 const situ::GateK &gate_consts(double beta)
@@ -260,7 +280,7 @@ const char *situ_glu_last_error(void) { return g_last_error.c_str(); }
 
 size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate, int64_t rw_rows)
 {
-    if (rows < 0 || intermediate < 0 || rows > (int64_t)0x7fffffff * 4)
+    if (rows < 0 || intermediate < 0 || rows > (int64_t)0x7fffffff)
         return 0;
     if (rw_rows == 1 && rows > 1)
         return (size_t)rows * sizeof(float);
@@ -268,7 +288,8 @@ size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate, int64_t 
 }
 
 // Exposed for tests: the root-window constants the kernels use for a beta:
-// out[0] = G*_f32, out[1] = half width, out[2..5] = c0..c3.
+// out[0] = G*_f32, out[1] = cubic half width, out[2..5] = c0..c3,
+// out[6] = quadratic half width.
 int situ_glu_gate_window(double beta, float *out)
 {
     g_last_error.clear();
@@ -283,6 +304,7 @@ int situ_glu_gate_window(double beta, float *out)
     out[3] = k.c1;
     out[4] = k.c2;
     out[5] = k.c3;
+    out[6] = k.win_hw2;
     return SITU_OK;
 }
 
@@ -317,9 +339,11 @@ int situ_glu_fwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     L.rows = rows;
     L.inter = (int)intermediate;
     L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
-    L.vec = aligned16(gate_up) && aligned16(out) && (intermediate * es) % 16 == 0;
+    L.vec = aligned16(gate_up) && aligned16(out) && (intermediate * es) % 16 == 0 &&
+            intermediate * 2 * es < ((int64_t)1 << 31);
     L.lb = linear_beta != nullptr;
     L.fast = beta == 4.0;
+    L.rows_per_block = rows_per_block_override();
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
     const int err = situ::launch_fwd(L, stream);
@@ -396,9 +420,11 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     L.rows = rows;
     L.inter = (int)intermediate;
     L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
-    L.vec = aligned16(gate_up) && aligned16(grad_out) && aligned16(d_gate_up) && (intermediate * es) % 16 == 0;
+    L.vec = aligned16(gate_up) && aligned16(grad_out) && aligned16(d_gate_up) &&
+            (intermediate * es) % 16 == 0 && intermediate * 2 * es < ((int64_t)1 << 31);
     L.lb = linear_beta != nullptr;
     L.fast = beta == 4.0;
+    L.rows_per_block = rows_per_block_override();
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
     const int err = situ::launch_bwd(L, stream);

@@ -8,27 +8,28 @@
 namespace situ {
 
 // Gate-branch constants for one beta (b1), computed on the host.
-//   e1 = exp(-2|G|/b1) = exp2(|G| * k1)
+//   e1 = exp(-2|G|/b1) = exp2(-|G| * k1)
 //   y1 = 2|G|/b1       = |G| * y1k    (argument of 1 - e1 = 1 - exp(-y1))
 // The root window: dT_g/dG vanishes at G* < 0, where its two terms cancel.
-// Inside |G - win_ghi| <= win_hw the kernels evaluate dT_g/dG as the cubic
-// c0 + c1 d + c2 d^2 + c3 d^3 in d = G - win_ghi (the Taylor expansion at the
-// fp32 number nearest G*) instead of the cancelling difference.
+// Inside |G - win_ghi| <= win_hw the fp32-io kernels evaluate dT_g/dG as the
+// cubic c0 + c1 d + c2 d^2 + c3 d^3 in d = G - win_ghi (the Taylor expansion
+// at the fp32 number nearest G*) instead of the cancelling difference; the
+// bf16-io kernels use the quadratic c0 + c1 d + c2 d^2 inside win_hw2.
 struct GateK {
     float beta1;
     float k1;
     float y1k;
     float win_ghi;
     float win_hw;
+    float win_hw2;
     float c0, c1, c2, c3;
 };
 
-// Up-branch constants (only used when linear_beta is given).
-//   v = exp(-2|U|/b2) = exp2(|U| * ku), y2 = 2|U|/b2 = |U| * y2k
+// Up-branch constant (only used when linear_beta is given):
+//   v = exp(-2|U|/b2) = exp2(-|U| * ku)
 struct UpK {
     float beta2;
     float ku;
-    float y2k;
 };
 
 enum { IO_F32 = 0, IO_BF16 = 1 };
@@ -45,6 +46,7 @@ struct FwdLaunch {
     int vec;              // 1: 128-bit path, 0: element path
     int lb;               // linear_beta given
     int fast;             // beta1 == 4 specialisation
+    int rows_per_block;   // 128-bit path, rows of one strip: rows per workgroup (0 = default)
     GateK gk;
     UpK uk;
 };
@@ -64,6 +66,7 @@ struct BwdLaunch {
     int vec;
     int lb;
     int fast;
+    int rows_per_block;   // 128-bit path, rows of one strip: rows per workgroup (0 = default)
     GateK gk;
     UpK uk;
 };

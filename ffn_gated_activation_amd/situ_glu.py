@@ -136,9 +136,10 @@ def situ_glu_abi_version() -> int:
 
 
 def situ_glu_gate_window(beta: float = 4.0):
-    """(G*_f32, half width, c0, c1, c2, c3) the kernels use near the root of dT_g/dG."""
+    """(G*_f32, cubic half width, c0, c1, c2, c3, quadratic half width): the
+    constants the kernels use near the root of dT_g/dG."""
     import ctypes
     lib = _capi.load()
-    out = (ctypes.c_float * 6)()
+    out = (ctypes.c_float * 7)()
     _capi.check(lib.situ_glu_gate_window(float(beta), out), lib)
     return tuple(float(v) for v in out)

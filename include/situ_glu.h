@@ -152,9 +152,11 @@ int situ_glu_abi_version(void);
  * for a given beta (host only, no device work).  There the two terms of
  * dT_g/dG cancel (Megatron-LM PR "Add SiTU-GLU through Transformer Engine",
  * section "Activation": T_g has its minimum at G*), so inside
- * |G - out[0]| <= out[1] the kernels evaluate dT_g/dG as
+ * |G - out[0]| <= out[1] the fp32-io kernels evaluate dT_g/dG as
  * out[2] + out[3] d + out[4] d^2 + out[5] d^3 with d = G - out[0]
- * (out[0] = G* rounded to fp32).  out must hold 6 floats.
+ * (out[0] = G* rounded to fp32), and inside |G - out[0]| <= out[6] the
+ * bf16-io kernels evaluate out[2] + out[3] d + out[4] d^2.  out must hold 7
+ * floats.
  * Returns SITU_OK or SITU_ERR_INVALID_ARG (bad beta, NULL out).
  */
 int situ_glu_gate_window(double beta, float *out);

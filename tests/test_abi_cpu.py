@@ -109,6 +109,7 @@ def test_bwd_rejects(lib, capi, kw):
 
 def test_unsupported_sizes(lib, capi):
     assert _fwd(lib, inter=1 << 30, rows=1, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+    assert _fwd(lib, rows=1 << 31, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
 
 
 def test_workspace_bytes(lib):
@@ -129,14 +130,14 @@ def test_python_layer_rejects_cpu_tensors():
 
 def test_gate_window_constants(capi, lib):
     """The root window the kernels use agrees with the oracle: G*_f32 is the
-    float nearest the oracle's root, and the cubic matches the oracle's
-    dT_g/dG inside the window to 1e-6 relative (the polynomial itself,
-    evaluated in double)."""
+    float nearest the oracle's root, the cubic (fp32 io) matches the oracle's
+    dT_g/dG inside its window to 1e-6 relative and the quadratic (bf16 io)
+    inside its window to 1e-4 (the polynomials evaluated in double)."""
     import oracle
-    out = (ctypes.c_float * 6)()
+    out = (ctypes.c_float * 7)()
     for beta in (4.0, 3.0, 1.0, 0.5, 2.0, 100.0, 1e4):
         assert lib.situ_glu_gate_window(beta, out) == 0
-        ghi, hw, c0, c1, c2, c3 = [float(v) for v in out]
+        ghi, hw, c0, c1, c2, c3, hw2 = [float(v) for v in out]
         lo, hi = -80.0, -1e-4
         for _ in range(200):
             mid = 0.5 * (lo + hi)
@@ -155,4 +156,13 @@ def test_gate_window_constants(capi, lib):
             # coefficients are rounded to fp32: allow their rounding too
             tol = 1e-6 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d) + abs(c3 * d ** 3))
             assert abs(p - t) <= tol, (beta, d, p, t)
+        # the bf16 kernels' quadratic: within 1e-4 of the term scale inside hw2
+        assert 0 < hw2 <= hw
+        for d in np.linspace(-hw2, hw2, 41):
+            g = ghi + d
+            p2 = c0 + d * (c1 + d * c2)
+            t = oracle.gate_grad(g, beta)
+            scale = abs(c1 * (g - root)) + 1e-300
+            tol = 1e-4 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d))
+            assert abs(p2 - t) <= tol, (beta, d, p2, t)
     assert lib.situ_glu_gate_window(-1.0, out) == capi.SITU_ERR_INVALID_ARG
