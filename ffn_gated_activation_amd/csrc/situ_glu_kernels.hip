@@ -37,17 +37,22 @@
 namespace situ {
 namespace {
 
+// 128-bit vectors in flight per lane and input stream; a wavefront's strip
+// is 64 lanes x unroll vectors of each half row.  Measured on MI355X: 4 for
+// the forward (2 input streams) and 2 for the backward (3 input streams,
+// which then fits in 64 VGPRs: 8 wavefronts per SIMD).
 #ifndef SITU_UNROLL_FWD
 #define SITU_UNROLL_FWD 4
 #endif
 #ifndef SITU_UNROLL_BWD
-#define SITU_UNROLL_BWD 4
+#define SITU_UNROLL_BWD 2
 #endif
-// 128-bit vectors in flight per lane and input stream, and the strip of a
-// wavefront (64 lanes x unroll vectors of each half row).
 constexpr int kUnrollFwd = SITU_UNROLL_FWD;
 constexpr int kUnrollBwd = SITU_UNROLL_BWD;
 constexpr int kMaxWaves = 16;           // wavefronts per workgroup
+#ifndef SITU_BWD_MIN_WAVES
+#define SITU_BWD_MIN_WAVES 8  // wavefronts per SIMD the backward must fit (<= 64 VGPRs)
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -151,29 +156,30 @@ __device__ __forceinline__ float load_rw(const void *rw, int rw_bf16, int64_t i)
 
 // ---------------------------------------------------------------- element math
 
-// s * (1 - exp(-y)) for y = z ln2 >= 0, given e = exp(-y) = 2^-z as rounded by
-// the exponential.  For small y the subtraction loses relative accuracy
-// (error ~ ulp(1)/y); there the Taylor series is used instead.  PRECISE
-// (fp32 io) keeps five terms below y = 1/16 (truncation < 2e-9 relative,
-// subtraction error above < 2e-6); otherwise two terms below y = 1/64
-// (< 5e-5 and < 1e-5), far inside half a bf16 ulp (2^-9).  The scale s is
-// folded into both branches: s (1 - e) = fma(-e, s, s).
-template <bool PRECISE>
+// s * (1 - exp(-y)) for y = zk z ln2 >= 0, given e = exp(-y) as rounded by the
+// exponential (zk is 1 or 2, a compile-time constant).  For small y the
+// subtraction 1 - e loses relative accuracy (v_exp_f32 is within 0.77 ulp, so
+// the error is ~5e-8/y); there the Taylor series of 1 - exp(-y) is used
+// instead.  PRECISE (fp32 io) keeps five terms below y = 1/16 (truncation
+// < 2e-9 relative, subtraction error above < 1e-6); otherwise the first term
+// below y = 2^-11 (truncation y/2 <= 2.4e-4, subtraction error above
+// <= 1e-4), both well inside half a bf16 ulp (2^-9).  The scale s rides on
+// both branches: s (1 - e) = fma(-e, s, s).
+template <bool PRECISE, int ZK>
 __device__ __forceinline__ float scaled_one_minus_exp2_neg(float z, float e, float s)
 {
     if (PRECISE) {
-        const float y = z * kLn2;
+        const float y = z * (ZK * kLn2);
         const float p = y * (1.0f - y * (0.5f - y * (1.0f / 6.0f - y * (1.0f / 24.0f - y * (1.0f / 120.0f)))));
         return y < 0.0625f ? s * p : fmaf(-e, s, s);
     } else {
-        // y (1 - y/2) = z (ln2 - z ln2^2 / 2)
-        const float p = z * fmaf(z, (-0.5f * kLn2 * kLn2) * s, kLn2 * s);
-        return z < (0.015625f / kLn2) ? p : fmaf(-e, s, s);
+        const float p = z * ((ZK * kLn2) * s);
+        return z < (0.00048828125f / (ZK * kLn2)) ? p : fmaf(-e, s, s);
     }
 }
 
 struct Gate {
-    float e1, e2, nt, A, B;
+    float e1, e2, nt;
     float sn_s;   // sgn(G) * sigmoid numerator: G < 0 ? -e2 : 1
     float snc_s;  // sgn(G) * sigmoid(-G) numerator: G < 0 ? -1 : e2
 };
@@ -193,9 +199,7 @@ __device__ __forceinline__ Gate gate_parts(float g, float ntscale, const GateK &
         const float h = ex2(a * (-0.5f * kLog2e));
         o.e2 = h * h;
     }
-    o.nt = scaled_one_minus_exp2_neg<PRECISE>(z, o.e1, ntscale);
-    o.A = 1.0f + o.e1;
-    o.B = 1.0f + o.e2;
+    o.nt = scaled_one_minus_exp2_neg<PRECISE, 1>(z, o.e1, ntscale);
     const bool neg = g < 0.0f;
     o.sn_s = neg ? -o.e2 : 1.0f;
     o.snc_s = neg ? -1.0f : o.e2;
@@ -207,14 +211,15 @@ template <bool LB, bool FAST, bool PRECISE>
 __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const GateK &gk, const UpK &uk)
 {
     const Gate t = gate_parts<FAST, PRECISE>(g, rscale, gk);
+    const float m = (1.0f + t.e2) + fmaf(t.e1, t.e2, t.e1);  // (1 + e1)(1 + e2)
     if (LB) {
         const float z = fabsf(u) * uk.ku;  // v = 2^-z = exp(-2|U|/b2)
         const float v = ex2(-z);
-        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE>(z, v, 1.0f), u);
-        const float q = rcp(t.A * t.B * (1.0f + v));
+        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 1>(z, v, 1.0f), u);
+        const float q = rcp(m * (1.0f + v));
         return (t.nt * t.sn_s) * (nu * q);
     } else {
-        const float q = rcp(t.A * t.B);
+        const float q = rcp(m);
         return (t.nt * t.sn_s) * (u * q);
     }
 }
@@ -239,6 +244,11 @@ struct BwdOut {
 };
 
 // cG = 4 r b2 (4 r without linear beta), cU = 4 r b1 (r b1 without).
+// With m = (1 + e1)(1 + e2) = A B, q = 1 / (m C), a1 = nt sn and X = go q:
+//   T_g / b1 = a1 q C,  T_u / b2 = nu q m,  T_u' / 4 = v (q m)^2,
+// and since q m C = 1:
+//   go T_g T_u / (b1 b2) = X a1 nu,  dU = X a1 v (q m) cU,
+//   dG = go nu (q m) (T_g' / 4) cG,  T_g' / 4 = |sn| br (q C)^2.
 template <bool LB, bool FAST, bool PRECISE>
 __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG, float cU,
                                            const GateK &gk, const UpK &uk)
@@ -247,32 +257,30 @@ __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG,
     const Gate t = gate_parts<FAST, PRECISE>(g, 1.0f, gk);
     // T_g' / (4 sn) * (A B)^2 = e1 B + (b1/4) sgn(G) (1 - e1^2) snc, e1 B = e1 + e1 e2
     const float om = FAST ? 1.0f - t.e2 : (0.25f * gk.beta1) * fmaf(-t.e1, t.e1, 1.0f);
-    const float br = fmaf(om, t.snc_s, fmaf(t.e1, t.e2, t.e1));
+    const float e1B = fmaf(t.e1, t.e2, t.e1);
+    const float br = fmaf(om, t.snc_s, e1B);
     const float sbr = fabsf(t.sn_s) * br;
+    const float m = (1.0f + t.e2) + e1B;
+    const float a1 = t.nt * t.sn_s;
     if (LB) {
         // exp(-2|U|/b2) as the square of exp(-|U|/b2): gradual underflow of T_u'
         const float z = fabsf(u) * (0.5f * uk.ku);
         const float h = ex2(-z);
         const float v = h * h;
-        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE>(2.0f * z, v, 1.0f), u);
+        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 2>(z, v, 1.0f), u);
         const float C = 1.0f + v;
-        const float m = t.A * t.B;
         const float q = rcp(m * C);
         const float iab = q * C;                 // 1 / (A B)
         const float ic = q * m;                  // 1 / C
-        const float tg = t.nt * t.sn_s * iab;    // T_g / b1
-        const float tu = nu * ic;                // T_u / b2
         const float tgp = gate_grad4_window<PRECISE>(g, sbr * (iab * iab), gk);  // T_g' / 4
-        const float tup = v * (ic * ic);         // T_u' / 4
-        const float z1 = go * tg;
-        o.p = z1 * tu;
-        o.du = z1 * tup * cU;
-        o.dg = go * tu * tgp * cG;
+        const float xa1 = (go * q) * a1;
+        o.p = xa1 * nu;
+        o.du = xa1 * v * ic * cU;
+        o.dg = go * nu * ic * tgp * cG;
     } else {
-        const float q = rcp(t.A * t.B);
-        const float tg = t.nt * t.sn_s * q;      // T_g / b1
+        const float q = rcp(m);
         const float tgp = gate_grad4_window<PRECISE>(g, sbr * (q * q), gk);
-        const float z1 = go * tg;
+        const float z1 = go * (a1 * q);          // go T_g / b1
         o.p = z1 * u;
         o.du = z1 * cU;
         o.dg = go * u * tgp * cG;
@@ -388,7 +396,7 @@ situ_glu_fwd_vec_kernel(const void *__restrict__ gate_up, const void *__restrict
 }
 
 template <int IO, bool LB, bool FAST, bool DR>
-__global__ void __launch_bounds__(64 * kMaxWaves)
+__global__ void __launch_bounds__(64 * kMaxWaves, SITU_BWD_MIN_WAVES)
 situ_glu_bwd_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
                         int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
                         void *__restrict__ d_rw, float *__restrict__ row_partials, int64_t rows, int inter,
