@@ -166,3 +166,11 @@ def test_gate_window_constants(capi, lib):
             tol = 1e-4 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d))
             assert abs(p2 - t) <= tol, (beta, d, p2, t)
     assert lib.situ_glu_gate_window(-1.0, out) == capi.SITU_ERR_INVALID_ARG
+
+
+def test_autograd_rejects_cpu_tensors():
+    import torch
+
+    from ffn_gated_activation_amd import weighted_situ
+    with pytest.raises(ValueError):
+        weighted_situ(torch.zeros(2, 8, requires_grad=True), torch.ones(2, 1))

@@ -1,0 +1,65 @@
+"""GPU parity on every element of the full-size workloads.
+
+The whole forward and backward run once on the GPU at the workload's full
+size, in the launch configuration the benchmark times; the outputs are then
+compared with the fp64 oracle chunk by chunk (each row depends only on its
+own inputs, so the oracle evaluates any block of rows on its own).  Same bar
+as test_gpu_parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from compare import assert_close, assert_dr_close
+from ref import oracle_results
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+CHUNK_ELEMS = 1 << 23   # elements (rows x intermediate) per oracle chunk
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name", ["top1_fwd", "routed_top8", "stress_sat", "dense_ffn"])
+def test_every_element_full_size(name):
+    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd
+    from ffn_gated_activation_amd.workloads import make_inputs
+    print(f"[full] {name}", flush=True)
+    x = make_inputs(name, device=DEV, seed=0)
+    gu, rw, go = x["gate_up"], x["routing_weights"], x["grad_out"]
+    beta, lb, want = x["beta"], x["linear_beta"], x["want_drw"]
+    y = situ_glu_fwd(gu, rw, beta, lb)
+    dgu = drw = None
+    if go is not None:
+        dgu, drw = situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want)
+    torch.cuda.synchronize()
+    rows, inter = y.shape
+    step = max(1, CHUNK_ELEMS // inter)
+    broadcast = rw.numel() == 1
+    worst = {"y": 0, "dG": 0, "dU": 0, "dr": 0.0}
+    for lo in range(0, rows, step):
+        hi = min(rows, lo + step)
+        rws = rw if broadcast else rw[lo:hi]
+        gos = None if go is None else go[lo:hi]
+        ref = oracle_results(gu[lo:hi], rws, gos, beta, lb, want and not broadcast,
+                             backward=go is not None)
+        tag = f"{name}[{lo}:{hi}]"
+        worst["y"] = max(worst["y"], assert_close(f"{tag} Y", y[lo:hi], ref["y"]))
+        if go is not None:
+            d = dgu[lo:hi]
+            worst["dG"] = max(worst["dG"], assert_close(f"{tag} dG", d[:, :inter], ref["dgu"][:, :inter],
+                                                         ref["dg_scale"]))
+            worst["dU"] = max(worst["dU"], assert_close(f"{tag} dU", d[:, inter:], ref["dgu"][:, inter:]))
+            if want and not broadcast:
+                worst["dr"] = max(worst["dr"], assert_dr_close(f"{tag} dr", drw[lo:hi].reshape(-1), ref["dr"],
+                                                               ref["dr_abs"]))
+    print(f"[full] {name} ok: max bf16 ulp Y {worst['y']} dG {worst['dG']} dU {worst['dU']}; "
+          f"max dr error / scale {worst['dr']:.2e}", flush=True)
+    del x, gu, rw, go, y, dgu, drw
+    torch.cuda.empty_cache()
