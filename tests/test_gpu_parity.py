@@ -97,6 +97,9 @@ SMALL = [
     ("stress_sat", 33, 520),     # 65 vectors per half row
     ("routed_top8", 24, 24),     # 3 vectors per half row: most lanes idle
     ("fp32_small", 37, 516),     # fp32 vector path with a ragged lane tail
+    ("routed_top8", 8, 40000),   # more strips than wavefronts per row: each walks several
+    ("fp32_small", 16, 4096),    # fp32 rows of several strips (LDS merge of dr)
+    ("stress_sat", 5, 65536),    # the longest rows: 16 wavefronts, 8192 vectors per half
 ]
 
 
