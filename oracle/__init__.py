@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
 leg of ``bench.py`` may import this package; the product path never does.  The
-arithmetic lives in ``situ_oracle.c`` (plain C, double precision, libm), which
-shares nothing with the HIP library.  This module only compiles it with gcc,
-loads it with ctypes and marshals numpy arrays.
+arithmetic lives in ``situ_oracle.c`` (the activation and its gradients) and
+``mx_oracle.c`` (MXFP8 block quantisation), plain C in double precision with
+libm, sharing nothing with the HIP library.  This module only compiles them
+with gcc, loads them with ctypes and marshals numpy arrays.
 
 Definitions followed (see the header of ``situ_oracle.c``):
   * Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine", section
@@ -30,6 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "situ_oracle.c")
+_MX_SRC = os.path.join(_HERE, "mx_oracle.c")
 _LIB = os.path.join(_HERE, "libsitu_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -37,11 +39,11 @@ _lib = None
 _dp = ctypes.POINTER(ctypes.c_double)
 
 
-def build(src: str = _SRC, out: str = _LIB) -> str:
+def build(src: str = _SRC, out: str = _LIB, mx_src: str = _MX_SRC) -> str:
     """Compile the oracle with gcc (no fast-math: IEEE double semantics)."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, mx_src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -70,6 +72,17 @@ def _bind(lib):
     lib.situ_oracle_bf16_bits_array.argtypes = [i64, _dp, ctypes.POINTER(ctypes.c_uint16)]
     lib.situ_oracle_f32_array.restype = None
     lib.situ_oracle_f32_array.argtypes = [i64, _dp, ctypes.POINTER(ctypes.c_float)]
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.mx_oracle_fp8_decode.restype = ctypes.c_double
+    lib.mx_oracle_fp8_decode.argtypes = [ctypes.c_uint8, ctypes.c_int]
+    lib.mx_oracle_fp8_encode.restype = ctypes.c_uint8
+    lib.mx_oracle_fp8_encode.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.mx_oracle_scale_code.restype = ctypes.c_int
+    lib.mx_oracle_scale_code.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.mx_oracle_quantize_block.restype = None
+    lib.mx_oracle_quantize_block.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p, u8p]
+    lib.mx_oracle_quantize_rows.restype = None
+    lib.mx_oracle_quantize_rows.argtypes = [i64, i64, _dp, ctypes.c_int, ctypes.c_int, u8p, u8p]
     return lib
 
 
@@ -222,3 +235,54 @@ def round_f32(x, lib=None) -> np.ndarray:
     out = np.empty(a.shape, dtype=np.float32)
     lib.situ_oracle_f32_array(a.size, _ptr(a), _ptr(out, ctypes.c_float))
     return out
+
+
+# ----------------------------------------------------------------- MXFP8
+
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+MX_SCALE_MODES = {"floor": 0, "ceil": 1}
+MX_BLOCK = 32
+
+
+def _fmt(fmt) -> int:
+    return FP8_FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _mode(mode) -> int:
+    return MX_SCALE_MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def fp8_decode(code: int, fmt="e4m3", lib=None) -> float:
+    """Value of an OFP8 code (E4M3 or E5M2)."""
+    return (lib or load()).mx_oracle_fp8_decode(int(code), _fmt(fmt))
+
+
+def fp8_encode(x: float, fmt="e4m3", lib=None) -> int:
+    """Nearest OFP8 code, ties to even, saturating at the largest finite value."""
+    return int((lib or load()).mx_oracle_fp8_encode(float(x), _fmt(fmt)))
+
+
+def mx_scale_code(amax: float, fmt="e4m3", mode="floor", lib=None) -> int:
+    """E8M0 scale code of a block with largest magnitude amax."""
+    return int((lib or load()).mx_oracle_scale_code(float(amax), _fmt(fmt), _mode(mode)))
+
+
+def mx_quantize(x, fmt="e4m3", mode="floor", threads: int = 1, lib=None):
+    """Blocks of 32 along each row of x [rows, cols] (fp64): (codes uint8
+    [rows, cols], scales uint8 [rows, ceil(cols / 32)])."""
+    lib = lib or load()
+    a = _as_f64(x)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    rows, cols = a.shape
+    nblk = -(-cols // MX_BLOCK)
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows, nblk), dtype=np.uint8)
+    u8 = ctypes.c_uint8
+
+    def run(lo, hi):
+        lib.mx_oracle_quantize_rows(hi - lo, cols, _ptr(a[lo:hi]), _fmt(fmt), _mode(mode),
+                                    _ptr(codes[lo:hi], u8), _ptr(scales[lo:hi], u8))
+
+    _run_blocks(run, rows, threads)
+    return codes, scales

@@ -75,3 +75,40 @@ def worked_cases():
             else:  # Y, dG, dU: exact rationals per row
                 cur[key] = [[Fraction(t) for t in row.split()] for row in rest.split(";")]
     return cases
+
+
+def _num(tok: str) -> float:
+    if tok.lower() == "nan":
+        return float("nan")
+    if "0x" in tok.lower():
+        return float.fromhex(tok)
+    return float(tok)
+
+
+def mx_blocks():
+    """Hand-worked MXFP8 blocks: dicts with name, fmt, mode, cols, values
+    (padded with zeros to cols), scales and codes (None when not given)."""
+    out = []
+    cur = None
+    with open(os.path.join(GOLDEN, "mx_blocks.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *toks = line.split()
+            if key == "block":
+                name, fmt, mode, cols = toks
+                cur = {"name": name, "fmt": fmt, "mode": mode, "cols": int(cols)}
+                out.append(cur)
+            elif key == "values":
+                v = [_num(t) for t in toks]
+                cur["values"] = v + [0.0] * (cur["cols"] - len(v))
+            elif key == "scales":
+                cur["scales"] = [int(t) for t in toks]
+            elif key == "codes":
+                if toks == ["-"]:
+                    cur["codes"] = None
+                else:
+                    c = [int(t, 16) for t in toks]
+                    cur["codes"] = c + [0] * (cur["cols"] - len(c))
+    return out

@@ -10,7 +10,11 @@ AssertionError when the oracle disagrees with:
   * the SiLU limit b1 -> infinity against torch's silu,
   * central finite differences of the oracle's own forward,
   * the exact linearity of Y in the routing weight,
-  * bfloat16 / fp32 rounding by torch and numpy.
+  * bfloat16 / fp32 rounding by torch and numpy,
+  * MXFP8: hand-worked blocks (tests/golden/mx_blocks.txt), torch's own
+    float8_e4m3fn / float8_e5m2 codecs, numpy's binary16 (whose top byte is
+    E5M2), exact rational rounding with Python's fractions, and the bounds
+    the scale rules imply.
 The same functions run against mutated copies of the oracle
 (test_oracle_mutants.py): every planted mistake must trip at least one pin.
 """
@@ -21,7 +25,7 @@ import math
 import numpy as np
 
 import oracle
-from golden_io import closed_forms, worked_cases
+from golden_io import closed_forms, mx_blocks, worked_cases
 
 # tribonacci constant: real root of t^3 = t^2 + t + 1 (Cardano)
 _TRIB = (1.0 + (19.0 + 3.0 * math.sqrt(33.0)) ** (1.0 / 3.0)
@@ -369,6 +373,168 @@ def pin_f32_rounding(lib):
     rng = np.random.default_rng(9)
     x = np.concatenate([rng.normal(0, 1, 5000), rng.normal(0, 1e-40, 500), rng.normal(0, 1e38, 500)])
     np.testing.assert_array_equal(oracle.round_f32(x, lib=lib), x.astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# MXFP8 (OCP OFP8 element formats, OCP MX v1.0 block scales)
+# --------------------------------------------------------------------------
+
+_FP8 = {"e4m3": dict(mbits=3, bias=7, maxv=448.0, emax=8),
+        "e5m2": dict(mbits=2, bias=15, maxv=57344.0, emax=15)}
+
+
+def pin_mx_golden_blocks(lib):
+    for b in mx_blocks():
+        codes, scales = oracle.mx_quantize(np.array([b["values"]]), b["fmt"], b["mode"], lib=lib)
+        assert scales[0].tolist() == b["scales"], f"{b['name']}: scales {scales[0].tolist()} != {b['scales']}"
+        if b["codes"] is not None:
+            got = [int(c) for c in codes[0]]
+            assert got == b["codes"], f"{b['name']}: codes {[hex(c) for c in got]}"
+
+
+def pin_fp8_decode_vs_torch(lib):
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    for fmt, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        want = codes.view(dt).to(torch.float64).numpy()
+        got = np.array([oracle.fp8_decode(c, fmt, lib=lib) for c in range(256)])
+        both_nan = np.isnan(want) & np.isnan(got)
+        assert np.array_equal(np.isnan(want), np.isnan(got)), f"{fmt}: NaN codes differ"
+        assert np.array_equal(got[~both_nan], want[~both_nan]), f"{fmt}: decoded values differ from torch"
+    # E5M2 is the upper byte of IEEE binary16
+    half = (np.arange(256, dtype=np.uint16) << 8).view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp8_decode(c, "e5m2", lib=lib) for c in range(256)])
+    fin = ~np.isnan(half)
+    assert np.array_equal(np.isnan(half), np.isnan(got)) and np.array_equal(got[fin], half[fin])
+    # hand facts
+    assert oracle.fp8_decode(0x7E, "e4m3", lib=lib) == 448.0
+    assert oracle.fp8_decode(0x01, "e4m3", lib=lib) == 2.0 ** -9
+    assert oracle.fp8_decode(0x08, "e4m3", lib=lib) == 2.0 ** -6
+    assert oracle.fp8_decode(0x38, "e4m3", lib=lib) == 1.0
+    assert oracle.fp8_decode(0x7B, "e5m2", lib=lib) == 57344.0
+    assert oracle.fp8_decode(0x01, "e5m2", lib=lib) == 2.0 ** -16
+
+
+def _fp8_points(fmt):
+    """fp32-exact test points: every finite value, every midpoint between
+    neighbours, their fp32 neighbours, and random fp32 values."""
+    p = _FP8[fmt]
+    vals = sorted({oracle.fp8_decode(c, fmt) for c in range(256)} - {float("nan")})
+    vals = [v for v in vals if math.isfinite(v) and v >= 0]
+    mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    pts = np.array(vals + mids, dtype=np.float32)
+    near = np.concatenate([np.nextafter(pts, np.float32(np.inf)), np.nextafter(pts, np.float32(0))])
+    rng = np.random.default_rng(17)
+    rnd = np.exp(rng.uniform(np.log(2.0 ** -(p["bias"] + p["mbits"] + 2)), np.log(p["maxv"]), 20000))
+    allp = np.concatenate([pts, near, rnd.astype(np.float32)])
+    return np.concatenate([allp, -allp]).astype(np.float32)
+
+
+def pin_fp8_encode_vs_torch(lib):
+    import torch
+    for fmt, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        x = _fp8_points(fmt)
+        # torch does not saturate: compare below the last rounding midpoint
+        lim = _FP8[fmt]["maxv"] * (1 + 2.0 ** -(_FP8[fmt]["mbits"] + 1))
+        x = x[np.abs(x) < lim]
+        want = torch.from_numpy(x).to(dt).view(torch.uint8).numpy()
+        got = np.array([oracle.fp8_encode(float(v), fmt, lib=lib) for v in x], dtype=np.uint8)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{fmt}: {bad.size} codes differ from torch, first x={x[bad[0]]!r}"
+
+
+def pin_fp8_encode_exact_rational(lib):
+    """Round to nearest, ties to even, by exact rational arithmetic: the
+    quantum of |x| is 2^(max(floor(log2|x|), 1 - bias) - mbits); Python's
+    round() of a Fraction rounds half to even."""
+    from fractions import Fraction
+    rng = np.random.default_rng(23)
+    for fmt, p in _FP8.items():
+        xs = list(_fp8_points(fmt)[::7]) + list(rng.normal(0, 3, 500))
+        for x in xs:
+            x = float(x)
+            a = Fraction(abs(x))
+            if a == 0:
+                want = 0.0
+            else:
+                e = max(math.floor(math.log2(a)), 1 - p["bias"])
+                # log2 of a Fraction near a power of two: settle the binade exactly
+                while a < Fraction(2) ** e and e > 1 - p["bias"]:
+                    e -= 1
+                while a >= Fraction(2) ** (e + 1):
+                    e += 1
+                q = Fraction(2) ** (e - p["mbits"])
+                want = float(min(round(a / q) * q, Fraction(p["maxv"])))
+            got = oracle.fp8_decode(oracle.fp8_encode(x, fmt, lib=lib), fmt, lib=lib)
+            assert abs(got) == want, f"{fmt}: encode({x!r}) decodes to {got!r}, want {want!r}"
+            assert got == 0 or math.copysign(1, got) == math.copysign(1, x), f"{fmt}: sign of {x!r}"
+
+
+def pin_fp8_encode_saturates(lib):
+    for fmt, p in _FP8.items():
+        mx = oracle.fp8_encode(p["maxv"], fmt, lib=lib)
+        for x in (p["maxv"] * 1.01, p["maxv"] * 2, 1e30, float("inf")):
+            assert oracle.fp8_encode(x, fmt, lib=lib) == mx, f"{fmt}: {x} must clamp to the largest value"
+            assert oracle.fp8_encode(-x, fmt, lib=lib) == mx | 0x80
+        assert oracle.fp8_decode(mx, fmt, lib=lib) == p["maxv"]
+
+
+def pin_mx_scale_rules(lib):
+    """floor: amax / X in [2^emax, 2^(emax+1)); ceil: amax / X in
+    (maxv / 2, maxv]; both clamped to the E8M0 range; hand values."""
+    hand = [("e4m3", "floor", 448.0, 127), ("e4m3", "floor", 1.0, 119), ("e4m3", "floor", 0.75, 118),
+            ("e4m3", "floor", 500.0, 127), ("e4m3", "floor", 512.0, 128), ("e4m3", "ceil", 448.0, 127),
+            ("e4m3", "ceil", 448.00001, 128), ("e4m3", "ceil", 1.0, 119), ("e4m3", "ceil", 1.75, 119),
+            ("e4m3", "ceil", 1.7500001, 120), ("e5m2", "floor", 57344.0, 127), ("e5m2", "floor", 1.0, 112),
+            ("e5m2", "ceil", 57344.0, 127), ("e5m2", "ceil", 57345.0, 128), ("e4m3", "floor", 0.0, 0),
+            ("e4m3", "ceil", 0.0, 0), ("e4m3", "floor", 2.0 ** -140, 0), ("e4m3", "floor", float("inf"), 255),
+            ("e4m3", "ceil", float("nan"), 255)]
+    for fmt, mode, amax, want in hand:
+        got = oracle.mx_scale_code(amax, fmt, mode, lib=lib)
+        assert got == want, f"scale({fmt}, {mode}, {amax!r}) = {got}, want {want}"
+    rng = np.random.default_rng(29)
+    for amax in np.exp(rng.uniform(-80, 80, 3000)):
+        for fmt, p in _FP8.items():
+            s = oracle.mx_scale_code(amax, fmt, "floor", lib=lib) - 127
+            if -127 < s < 127:
+                t = amax / 2.0 ** s
+                assert 2.0 ** p["emax"] <= t < 2.0 ** (p["emax"] + 1), (fmt, amax, s)
+            s = oracle.mx_scale_code(amax, fmt, "ceil", lib=lib) - 127
+            if -127 < s < 127:
+                t = amax / 2.0 ** s
+                assert p["maxv"] / 2 < t <= p["maxv"], (fmt, amax, s)
+
+
+def pin_mx_block_properties(lib):
+    """Random rows: each block's scale depends only on its own 32 values;
+    ceil mode never saturates; every dequantised value lies within half a
+    quantum of V / X (or at the clamp in floor mode)."""
+    rng = np.random.default_rng(31)
+    cols = 32 * 5 + 7
+    x = rng.normal(0, 1, (6, cols)) * np.exp(rng.uniform(-20, 20, (6, 1)))
+    x[2, 40] = 0.0
+    for fmt, p in _FP8.items():
+        for mode in ("floor", "ceil"):
+            codes, scales = oracle.mx_quantize(x, fmt, mode, lib=lib)
+            assert scales.shape == (6, 6) and codes.shape == x.shape
+            y = x.copy()
+            y[:, 33] *= 1e6           # touches block 1 only (and makes it the row's largest)
+            c2, s2 = oracle.mx_quantize(y, fmt, mode, lib=lib)
+            assert np.array_equal(np.delete(s2, 1, axis=1), np.delete(scales, 1, axis=1))
+            assert np.array_equal(np.delete(c2, np.s_[32:64], axis=1), np.delete(codes, np.s_[32:64], axis=1))
+            for i in range(x.shape[0]):
+                for j in range(cols):
+                    b = j // 32
+                    X = 2.0 ** (int(scales[i, b]) - 127)
+                    v = x[i, j] / X
+                    d = oracle.fp8_decode(int(codes[i, j]), fmt, lib=lib)
+                    if abs(v) >= p["maxv"]:
+                        assert mode == "floor" or abs(v) == p["maxv"], (fmt, mode, i, j)
+                        assert abs(d) == p["maxv"]
+                        continue
+                    e = max(math.floor(math.log2(abs(v))) if v else 0, 1 - p["bias"])
+                    q = 2.0 ** (e - p["mbits"])
+                    assert abs(d - v) <= q / 2, (fmt, mode, i, j, v, d)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

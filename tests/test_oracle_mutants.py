@@ -1,7 +1,8 @@
 """Planted mistakes in the oracle must be caught by the pins.
 
-Each mutant is a copy of oracle/situ_oracle.c with one plausible slip (a
-dropped term, a wrong sign, a swapped operand or index, the wrong rounding),
+Each mutant is a copy of oracle/situ_oracle.c or oracle/mx_oracle.c with one
+plausible slip (a dropped term, a wrong sign, a swapped operand or index, the
+wrong rounding, a wrong format constant),
 compiled with gcc into a temporary directory.  The mistakes are planted in the
 CPU oracle only; no GPU code is involved.  A mutant that passes every pin
 would mean the pins cannot see that kind of error.
@@ -15,6 +16,7 @@ import oracle
 from oracle_pins import ALL_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "situ_oracle.c")
+MX_SRC = os.path.join(os.path.dirname(oracle.__file__), "mx_oracle.c")
 
 MUTANTS = {
     "sech2_as_one_minus_tanh2": (
@@ -62,19 +64,44 @@ MUTANTS = {
     "bf16_one_bit_short": ("double quantum = ldexp(1.0, e - 7);", "double quantum = ldexp(1.0, e - 6);"),
 }
 
+MX_MUTANTS = {
+    "e4m3_bias_8": ("f.mbits = 3; f.bias = 7;", "f.mbits = 3; f.bias = 8;"),
+    "e5m2_bias_16": ("f.mbits = 2; f.bias = 15;", "f.mbits = 2; f.bias = 16;"),
+    "e4m3_emax_7": ("f.max_finite = 448.0; f.emax = 8;", "f.max_finite = 448.0; f.emax = 7;"),
+    "e4m3_max_480": ("f.max_finite = 448.0;", "f.max_finite = 480.0;"),
+    "subnormal_exponent_off_by_one": ("ldexp((double)m, 1 - f.bias - f.mbits)", "ldexp((double)m, -f.bias - f.mbits)"),
+    "ties_away_from_zero": ("(above == below && ((lo + 1) & 1) == 0)", "(above == below)"),
+    "ties_toward_zero": ("if (above < below || (above == below && ((lo + 1) & 1) == 0))", "if (above < below)"),
+    "truncates": ("        if (above < below || (above == below && ((lo + 1) & 1) == 0))\n            pick = lo + 1;\n", ""),
+    "no_saturation_nan": ("        return (uint8_t)(sign | f.max_code);", "        return (uint8_t)(sign | 0x7f);"),
+    "drops_sign": ("uint8_t sign = signbit(x) ? 0x80 : 0x00;", "uint8_t sign = 0x00;"),
+    "floor_scale_rounds_up": ("s = (e2 - 1) - f.emax;            /* floor", "s = e2 - f.emax;            /* floor"),
+    "ceil_mode_is_floor": ("        while (amax > ldexp(f.max_finite, s))\n            ++s;\n", ""),
+    "scale_divides_wrong_way": ("mx_oracle_fp8_encode(ldexp(v[i], -(sc - 127)), fmt)", "mx_oracle_fp8_encode(ldexp(v[i], sc - 127), fmt)"),
+    "scale_no_low_clamp": ("    if (s < -127)\n        s = -127;\n", ""),
+    "nan_block_finite_scale": ("int sc = nonfinite ? 255 : mx_oracle_scale_code", "int sc = nonfinite ? 254 : mx_oracle_scale_code"),
+    "block_spans_rest_of_row": ("int n = (int)(cols - j0 < MX_BLOCK ? cols - j0 : MX_BLOCK);", "int n = (int)(cols - j0);"),
+    "amax_signed": ("else if (fabs(v[i]) > amax)\n            amax = fabs(v[i]);", "else if (v[i] > amax)\n            amax = v[i];"),
+    "scale_index_transposed": ("scales + i * nblk + b);", "scales + b * rows + i);"),
+}
+
 
 def _build_mutant(name, tmp):
-    old, new = MUTANTS[name]
-    with open(SRC) as f:
+    mx = name in MX_MUTANTS
+    old, new = (MX_MUTANTS if mx else MUTANTS)[name]
+    with open(MX_SRC if mx else SRC) as f:
         text = f.read()
     assert text.count(old) == 1, f"mutation site for {name} not unique/found"
     path = os.path.join(tmp, f"m_{name}.c")
     with open(path, "w") as f:
         f.write(text.replace(old, new))
-    return oracle.build(src=path, out=os.path.join(tmp, f"libm_{name}.so"))
+    out = os.path.join(tmp, f"libm_{name}.so")
+    if mx:
+        return oracle.build(mx_src=path, out=out)
+    return oracle.build(src=path, out=out)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(MX_MUTANTS))
 def test_mutant_is_caught(name):
     with tempfile.TemporaryDirectory() as tmp:
         lib = oracle.load(_build_mutant(name, tmp))
