@@ -5,7 +5,8 @@
 
 One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
-inputs already resident in HBM.  W untimed steps, then K timed steps between
+inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
+forward with MXFP8 output instead (forward only).  W untimed steps, then K timed steps between
 two device synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
@@ -34,16 +35,22 @@ if ROOT not in sys.path:
 
 METRIC = "SiTU-GLU fwd+bwd achieved HBM GB/s (% of MI355X peak) and rows/s, bf16"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "ffn_gated_activation_amd", "csrc", "situ_glu_kernels.hip")
+CSRC = os.path.join(ROOT, "ffn_gated_activation_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_kernels.hip")
+MX_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_mx.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _kernel_source_hash(path: str = KERNEL_SOURCE) -> str:
+    """sha256 of a kernel source and the device header it includes."""
+    h = hashlib.sha256()
+    for p in (path, os.path.join(CSRC, "situ_glu_device.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def _traffic(workload: str, kernel: str):
+def _traffic(workload: str, kernel: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel source changed since it was taken."""
     path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
@@ -51,7 +58,7 @@ def _traffic(workload: str, kernel: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != _kernel_source_hash():
+    if rec.get("kernel_source_sha256") != _kernel_source_hash(source):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -70,16 +77,21 @@ def _cpu_baseline(workload: str, sample_rows: int) -> dict:
     gu = x["gate_up"].double().numpy()
     rw = x["routing_weights"].double().numpy()
     go = x["grad_out"].double().numpy() if x["grad_out"] is not None else None
+    mx = x["workload"].mx
     t0 = time.perf_counter()
-    oracle.forward(gu, rw, x["beta"], x["linear_beta"], threads=cores)
+    y = oracle.forward(gu, rw, x["beta"], x["linear_beta"], threads=cores)
+    if mx:
+        oracle.mx_quantize(y, mx, "floor", threads=cores)
     if go is not None:
         oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"],
                         want_scales=False, threads=cores)
     dt = time.perf_counter() - t0
     b = algorithmic_bytes(workload, rows=sample_rows)["total"]
+    what = ("fp64 forward + MXFP8 quantisation" if mx else
+            "fp64 forward+backward" if go is not None else "fp64 forward")
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{workload} recipe, first {sample_rows} rows (seed 0, drawn on the host), "
-                      f"fp64 forward+backward, {dt:.2f} s wall",
+                      f"{what}, {dt:.2f} s wall",
             "rows_per_s": round(sample_rows / dt, 1)}
 
 
@@ -90,7 +102,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="routed_top8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=32768)
+    ap.add_argument("--cpu-sample-rows", type=int, default=65536,
+                    help="rows of the CPU-oracle sample (capped at the workload's rows)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration runs)")
     args = ap.parse_args(argv)
@@ -102,7 +115,7 @@ def main(argv=None) -> int:
 
     import torch
 
-    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd
+    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd, situ_glu_fwd_mxfp8
     from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
 
     if not torch.cuda.is_available():
@@ -114,7 +127,11 @@ def main(argv=None) -> int:
     x = make_inputs(args.workload, device=dev, seed=0)
     gu, rw, go = x["gate_up"], x["routing_weights"], x["grad_out"]
     beta, lb, want = x["beta"], x["linear_beta"], x["want_drw"]
-    y = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
+    if w.mx:
+        codes = torch.empty(w.rows, w.inter, dtype=torch.uint8, device=dev)
+        scales = torch.empty(w.rows, -(-w.inter // 32), dtype=torch.uint8, device=dev)
+    else:
+        y = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
     dgu = torch.empty_like(gu) if w.backward else None
     drw = torch.empty_like(rw) if want else None
     torch.cuda.synchronize()
@@ -122,7 +139,10 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        situ_glu_fwd(gu, rw, beta, lb, out=y)
+        if w.mx:
+            situ_glu_fwd_mxfp8(gu, rw, beta, lb, w.mx, "floor", codes=codes, scales=scales)
+        else:
+            situ_glu_fwd(gu, rw, beta, lb, out=y)
         if ev is not None:
             ev[1].record()
         if w.backward:
@@ -164,7 +184,9 @@ def main(argv=None) -> int:
     dom_bytes = ab[dom]
     dom_ms = bwd_ms if w.backward else fwd_ms
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    kname = "situ_glu_bwd_kernel" if w.backward else "situ_glu_fwd_kernel"
+    kname = ("situ_glu_bwd_kernel" if w.backward else
+             "situ_glu_fwd_mx_kernel" if w.mx else "situ_glu_fwd_kernel")
+    src = MX_KERNEL_SOURCE if (w.mx and not w.backward) else KERNEL_SOURCE
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -180,7 +202,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rows": w.rows,
                    "intermediate": w.inter, "beta": w.beta, "linear_beta": w.linear_beta,
-                   "passes": "fwd+bwd" + ("+d_routing_weights" if want else "") if w.backward else "fwd",
+                   "passes": ("fwd+bwd" + ("+d_routing_weights" if want else "") if w.backward else
+                              f"fwd (MXFP8 {w.mx} output)" if w.mx else "fwd"),
                    "algorithmic_bytes_per_step": ab["total"]},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(w.rows / (ms_per_step / 1e3), 1),
@@ -192,7 +215,7 @@ def main(argv=None) -> int:
         },
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic(args.workload, dom)},
+                     "traffic": _traffic(args.workload, dom, src)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

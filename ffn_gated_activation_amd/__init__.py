@@ -10,12 +10,14 @@ from .situ_glu import (  # noqa: F401
     situ_glu_bwd,
     situ_glu_bwd_workspace_bytes,
     situ_glu_fwd,
+    situ_glu_fwd_mxfp8,
     situ_glu_gate_window,
     situ_glu_last_error,
+    situ_glu_mx_quantize,
 )
 from ._capi import SituGluError  # noqa: F401
 from .autograd import WeightedSiTUFunction, weighted_situ  # noqa: F401
 
 __all__ = ["situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes", "situ_glu_last_error",
-           "situ_glu_abi_version", "situ_glu_gate_window", "SituGluError", "WeightedSiTUFunction",
-           "weighted_situ"]
+           "situ_glu_abi_version", "situ_glu_gate_window", "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize",
+           "SituGluError", "WeightedSiTUFunction", "weighted_situ"]

@@ -20,11 +20,17 @@ SITU_ERR_UNSUPPORTED = 2
 SITU_ERR_DEVICE = 3
 SITU_DTYPE_F32 = 0
 SITU_DTYPE_BF16 = 1
-ABI_VERSION = 1
+SITU_FP8_E4M3 = 0
+SITU_FP8_E5M2 = 1
+SITU_MX_SCALE_FLOOR = 0
+SITU_MX_SCALE_CEIL = 1
+SITU_MX_BLOCK = 32
+ABI_VERSION = 2
 
 # every symbol include/situ_glu.h declares
 EXPORTED = ("situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes",
-            "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window")
+            "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window",
+            "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize")
 
 
 class SituGluError(RuntimeError):
@@ -52,6 +58,10 @@ def _bind(lib):
     lib.situ_glu_abi_version.argtypes = []
     lib.situ_glu_gate_window.restype = i32
     lib.situ_glu_gate_window.argtypes = [dbl, ctypes.POINTER(ctypes.c_float)]
+    lib.situ_glu_fwd_mxfp8.restype = i32
+    lib.situ_glu_fwd_mxfp8.argtypes = [vp, i32, i64, i64, vp, i32, i64, dbl, dblp, i32, i32, vp, vp, vp]
+    lib.situ_glu_mx_quantize.restype = i32
+    lib.situ_glu_mx_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
     return lib
 
 

@@ -3,8 +3,9 @@
     python -m ffn_gated_activation_amd.build
 
 The host API (csrc/situ_glu_api.cpp, plain C++) is compiled with g++, the
-kernels (csrc/situ_glu_kernels.hip) with hipcc for gfx950, and both are linked
-into ffn_gated_activation_amd/libsitu_glu.so.
+kernels (csrc/situ_glu_kernels.hip: forward and backward; csrc/situ_glu_mx.hip:
+MXFP8 forward and block quantiser) with hipcc for gfx950, in parallel, and all
+are linked into ffn_gated_activation_amd/libsitu_glu.so.
 """
 from __future__ import annotations
 
@@ -44,17 +45,31 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
+HIP_SOURCES = ("situ_glu_kernels.hip", "situ_glu_mx.hip")
+
+
 def build_library(verbose: bool = False, extra_hipcc: list[str] | None = None, out: str = LIB,
                   build_dir: str = BUILD) -> str:
     os.makedirs(build_dir, exist_ok=True)
     api_o = os.path.join(build_dir, "situ_glu_api.o")
-    ker_o = os.path.join(build_dir, "situ_glu_kernels.o")
-    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-          os.path.join(CSRC, "situ_glu_api.cpp"), "-o", api_o], verbose)
-    _run([_hipcc(), *HIPCC_FLAGS, *(extra_hipcc or []), "-I", INCLUDE, "-I", CSRC, "-c",
-          os.path.join(CSRC, "situ_glu_kernels.hip"), "-o", ker_o], verbose)
+    cmds = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+             os.path.join(CSRC, "situ_glu_api.cpp"), "-o", api_o]]
+    objs = [api_o]
+    for src in HIP_SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        cmds.append([_hipcc(), *HIPCC_FLAGS, *(extra_hipcc or []), "-I", INCLUDE, "-I", CSRC, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
+    failed = [cmd for cmd, p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = out + ".tmp%d" % os.getpid()
-    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o], verbose)
+    _run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, out)
     return out
 

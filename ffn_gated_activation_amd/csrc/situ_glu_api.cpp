@@ -87,6 +87,20 @@ int check_common(const void *gate_up, int io_dtype, int64_t rows, int64_t inter,
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_mx(int fp8_format, int scale_mode)
+{
+    if (fp8_format != SITU_FP8_E4M3 && fp8_format != SITU_FP8_E5M2)
+        return fail(SITU_ERR_INVALID_ARG, "fp8_format %d is not SITU_FP8_E4M3 (0) or SITU_FP8_E5M2 (1)",
+                    fp8_format);
+    if (scale_mode != SITU_MX_SCALE_FLOOR && scale_mode != SITU_MX_SCALE_CEIL)
+        return fail(SITU_ERR_INVALID_ARG,
+                    "scale_mode %d is not SITU_MX_SCALE_FLOOR (0) or SITU_MX_SCALE_CEIL (1)", scale_mode);
+    return SITU_OK;
+}
+
+int64_t mx_blocks(int64_t cols) { return (cols + SITU_MX_BLOCK - 1) / SITU_MX_BLOCK; }
 
 }  // namespace
 
@@ -430,6 +444,113 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     const int err = situ::launch_bwd(L, stream);
     if (err)
         return fail(SITU_ERR_DEVICE, "backward launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
+int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                       const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                       const double *linear_beta, int fp8_format, int scale_mode, void *codes, void *scales,
+                       void *stream)
+{
+    g_last_error.clear();
+    int rc = check_common(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows,
+                          beta, linear_beta);
+    if (rc)
+        return rc;
+    if ((rc = check_mx(fp8_format, scale_mode)))
+        return rc;
+    if (rows == 0 || intermediate == 0)
+        return SITU_OK;
+    if (!codes)
+        return fail(SITU_ERR_INVALID_ARG, "codes is NULL");
+    if (!scales)
+        return fail(SITU_ERR_INVALID_ARG, "scales is NULL");
+    const int64_t es = dtype_bytes(io_dtype);
+    const Range o_codes = range("codes", codes, rows * intermediate);
+    const Range o_scales = range("scales", scales, rows * mx_blocks(intermediate));
+    const Range ins[] = {range("gate_up", gate_up, rows * intermediate * 2 * es),
+                         range("routing_weights", routing_weights, rw_rows * dtype_bytes(rw_dtype))};
+    for (const Range &i : ins)
+        if (overlaps(o_codes, i) || overlaps(o_scales, i))
+            return fail(SITU_ERR_INVALID_ARG, "an output overlaps input %s", i.name);
+    if (overlaps(o_codes, o_scales))
+        return fail(SITU_ERR_INVALID_ARG, "codes and scales overlap");
+
+    situ::FwdMxLaunch L{};
+    L.gate_up = gate_up;
+    L.rw = routing_weights;
+    L.rw_bf16 = rw_dtype == SITU_DTYPE_BF16;
+    L.rw_stride = rw_rows == rows ? 1 : 0;
+    L.codes = codes;
+    L.scales = scales;
+    L.rows = rows;
+    L.inter = (int)intermediate;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = aligned16(gate_up) && (intermediate * es) % 16 == 0 && intermediate * 2 * es < ((int64_t)1 << 31) &&
+            aligned_to(codes, io_dtype == SITU_DTYPE_BF16 ? 8 : 4);
+    L.lb = linear_beta != nullptr;
+    L.fast = beta == 4.0;
+    L.fmt = fp8_format == SITU_FP8_E5M2 ? situ::FP8_E5M2 : situ::FP8_E4M3;
+    L.ceil_mode = scale_mode == SITU_MX_SCALE_CEIL;
+    L.rows_per_block = rows_per_block_override();
+    L.gk = gate_consts(beta);
+    L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    const int err = situ::launch_fwd_mx(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "MXFP8 forward launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
+int situ_glu_mx_quantize(const void *x, int io_dtype, int64_t rows, int64_t cols, int fp8_format,
+                         int scale_mode, void *codes, void *scales, void *stream)
+{
+    g_last_error.clear();
+    if (!dtype_ok(io_dtype))
+        return fail(SITU_ERR_INVALID_ARG, "io_dtype %d is not SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1)", io_dtype);
+    int rc = check_mx(fp8_format, scale_mode);
+    if (rc)
+        return rc;
+    if (rows < 0 || cols < 0)
+        return fail(SITU_ERR_INVALID_ARG, "negative size (rows=%lld, cols=%lld)", (long long)rows,
+                    (long long)cols);
+    if (cols > (int64_t)0x3fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "cols %lld exceeds 2^30 - 1", (long long)cols);
+    if (rows > (int64_t)0x7fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "rows %lld exceeds 2^31 - 1", (long long)rows);
+    if (rows == 0 || cols == 0)
+        return SITU_OK;
+    const int64_t es = dtype_bytes(io_dtype);
+    if (!x)
+        return fail(SITU_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned_to(x, (uintptr_t)es))
+        return fail(SITU_ERR_INVALID_ARG, "x is not aligned to its element size");
+    if (!codes)
+        return fail(SITU_ERR_INVALID_ARG, "codes is NULL");
+    if (!scales)
+        return fail(SITU_ERR_INVALID_ARG, "scales is NULL");
+    const Range in_x = range("x", x, rows * cols * es);
+    const Range o_codes = range("codes", codes, rows * cols);
+    const Range o_scales = range("scales", scales, rows * mx_blocks(cols));
+    if (overlaps(o_codes, in_x) || overlaps(o_scales, in_x))
+        return fail(SITU_ERR_INVALID_ARG, "an output overlaps input x");
+    if (overlaps(o_codes, o_scales))
+        return fail(SITU_ERR_INVALID_ARG, "codes and scales overlap");
+
+    situ::MxQuantLaunch L{};
+    L.x = x;
+    L.codes = codes;
+    L.scales = scales;
+    L.rows = rows;
+    L.cols = (int)cols;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = aligned16(x) && (cols * es) % 16 == 0 && cols * es < ((int64_t)1 << 31) &&
+            aligned_to(codes, io_dtype == SITU_DTYPE_BF16 ? 8 : 4);
+    L.fmt = fp8_format == SITU_FP8_E5M2 ? situ::FP8_E5M2 : situ::FP8_E4M3;
+    L.ceil_mode = scale_mode == SITU_MX_SCALE_CEIL;
+    L.rows_per_block = rows_per_block_override();
+    const int err = situ::launch_mx_quant(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "MXFP8 quantiser launch failed: %s", situ::device_error_string(err));
     return SITU_OK;
 }
 

@@ -71,9 +71,49 @@ struct BwdLaunch {
     UpK uk;
 };
 
+enum { FP8_E4M3 = 0, FP8_E5M2 = 1 };
+
+// Forward with MXFP8 output: codes [rows, inter] bytes, scales
+// [rows, ceil(inter / 32)] bytes.
+struct FwdMxLaunch {
+    const void *gate_up;
+    const void *rw;
+    int rw_bf16;
+    int64_t rw_stride;
+    void *codes;
+    void *scales;
+    int64_t rows;
+    int inter;
+    int io;
+    int vec;              // 1: 128-bit loads, 8-byte (bf16) / 4-byte (fp32) code stores
+    int lb;
+    int fast;
+    int fmt;              // FP8_E4M3 / FP8_E5M2
+    int ceil_mode;        // 0: floor(log2 amax) - emax, 1: no element saturates
+    int rows_per_block;
+    GateK gk;
+    UpK uk;
+};
+
+// MXFP8 quantisation of x [rows, cols] (io dtype).
+struct MxQuantLaunch {
+    const void *x;
+    void *codes;
+    void *scales;
+    int64_t rows;
+    int cols;
+    int io;
+    int vec;
+    int fmt;
+    int ceil_mode;
+    int rows_per_block;
+};
+
 // Enqueue the kernels; return the hipError_t of the launches (0 = success).
 int launch_fwd(const FwdLaunch &L, void *stream);
 int launch_bwd(const BwdLaunch &L, void *stream);
+int launch_fwd_mx(const FwdMxLaunch &L, void *stream);
+int launch_mx_quant(const MxQuantLaunch &L, void *stream);
 // Zero `bytes` bytes at device pointer p with a fill kernel.
 int launch_zero(void *p, int64_t bytes, void *stream);
 const char *device_error_string(int err);

@@ -1,0 +1,400 @@
+// MXFP8 output of the weighted SiTU-GLU forward for CDNA4 (gfx950), and the
+// same block quantiser on its own.
+//
+// The Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine" (section
+// "Validation") runs the activation of routed and shared experts under MXFP8
+// block scaling: the activation's output is consumed as MXFP8 by the next
+// projection.  Here the forward writes that form directly, so Y never exists
+// in 16 or 32 bits in HBM.  Format (OCP Microscaling Formats (MX) v1.0 with
+// the OCP 8-bit floating point element formats):
+//   - each row is cut into blocks of 32 consecutive values (the last block of
+//     a row may be shorter); each block has one E8M0 scale X = 2^s, stored as
+//     the byte s + 127 (255 = NaN);
+//   - scale mode floor: s = floor(log2(amax)) - emax_elem (8 for E4M3, 15 for
+//     E5M2), the MX definition; mode ceil: the smallest s with
+//     amax <= max_finite * 2^s, so that no element saturates; s is clamped to
+//     [-127, 127] (an all-zero block gets s = -127);
+//   - element i is Y_i / X rounded to nearest even in E4M3 or E5M2, with
+//     magnitudes past the largest finite value clamped to it;
+//   - a block holding a NaN or an infinity gets the NaN scale (the element
+//     bytes of such a block carry no value).
+//
+// Layout: codes [rows, cols] bytes (row major, one byte per value), scales
+// [rows, ceil(cols / 32)] bytes.
+//
+// Work decomposition as the bf16 forward: strips of 64 lanes x 4 128-bit
+// vectors per wavefront.  A lane holds 8 (bf16) or 4 (fp32) consecutive
+// values of a vector, so a block of 32 is 4 or 8 neighbouring lanes: their
+// largest magnitude meets through DPP lane swaps, inside the quad (and the
+// half row for 8 lanes).  Values are converted two at a time by gfx950's
+// scaled fp32 -> fp8 conversion, which divides by the power of two in its
+// scale operand's exponent field (the E8M0 byte itself, shifted into place)
+// and rounds to nearest even; floor mode clamps to the largest finite
+// value first.  Measured on MI355X, integer, compare and select
+// instructions issue at about two thirds the rate of fp32 multiply-add, and
+// the conversions at less than half: the instruction choices below follow
+// those rates.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "situ_glu_device.h"
+#include "situ_glu_internal.h"
+
+namespace situ {
+namespace {
+
+constexpr int kMxBlock = 32;
+constexpr int kUnrollMx = 4;   // 128-bit vectors in flight per lane and input stream
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum { MX_FLOOR = 0, MX_CEIL = 1 };
+
+template <int FMT> struct Fp8;
+template <> struct Fp8<FP8_E4M3> {
+    static constexpr int kEmax = 8;         // largest finite value 1.75 * 2^8 = 448
+    // (a, b) / 2^(exponent field of scale - 127), rounded to nearest even,
+    // into bytes 0, 1 (lo) or 2, 3 (hi) of old; no saturation (E4M3
+    // overflow gives NaN)
+    __device__ static uint32_t lo(float a, float b, float scale, uint32_t old)
+    {
+        return bits(__builtin_amdgcn_cvt_scalef32_pk_fp8_f32(vec(old), a, b, scale, false));
+    }
+    __device__ static uint32_t hi(float a, float b, float scale, uint32_t old)
+    {
+        return bits(__builtin_amdgcn_cvt_scalef32_pk_fp8_f32(vec(old), a, b, scale, true));
+    }
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    __device__ static v2i16 vec(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
+    __device__ static uint32_t bits(v2i16 x) { return __builtin_bit_cast(uint32_t, x); }
+};
+template <> struct Fp8<FP8_E5M2> {
+    static constexpr int kEmax = 15;        // largest finite value 1.75 * 2^15 = 57344
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    __device__ static uint32_t lo(float a, float b, float scale, uint32_t old)
+    {
+        return bits(__builtin_amdgcn_cvt_scalef32_pk_bf8_f32(vec(old), a, b, scale, false));
+    }
+    __device__ static uint32_t hi(float a, float b, float scale, uint32_t old)
+    {
+        return bits(__builtin_amdgcn_cvt_scalef32_pk_bf8_f32(vec(old), a, b, scale, true));
+    }
+    __device__ static v2i16 vec(uint32_t x) { return __builtin_bit_cast(v2i16, x); }
+    __device__ static uint32_t bits(v2i16 x) { return __builtin_bit_cast(uint32_t, x); }
+};
+
+// Bit pattern of the largest magnitude of E values.  With the sign cleared,
+// the unsigned order of float bit patterns is the order of magnitudes, with
+// infinity above every finite value and NaN above infinity: one integer max
+// yields a pattern >= 0x7f800000 exactly when a value is infinite or NaN.
+template <int E>
+__device__ __forceinline__ uint32_t lane_amax_bits(const float *y)
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        m = max(m, __float_as_uint(y[e]) & 0x7fffffffu);
+    return m;
+}
+
+// E8M0 code of a block from the bit pattern of its largest magnitude (at or
+// above 0x7f800000 for a block with a NaN or an infinity: NaN scale).  With
+// amax = 1.f * 2^(eb - 127) (eb the biased exponent), floor gives
+// s + 127 = eb - emax.  max_finite = 1.75 * 2^emax, so ceil adds one exactly
+// when the fraction exceeds 0.75: adding 0x1fffff carries into the exponent
+// field exactly then.  Zero and subnormal amax (eb = 0) fall below s = -127
+// and clamp to code 0; finite codes stay <= 247.
+template <int FMT, int MODE>
+__device__ __forceinline__ uint32_t scale_code(uint32_t amax_bits)
+{
+    const uint32_t adj = MODE == MX_CEIL ? amax_bits + 0x1fffffu : amax_bits;
+    const int c = (int)(adj >> 23) - Fp8<FMT>::kEmax;
+    return amax_bits >= 0x7f800000u ? 255u : (uint32_t)max(c, 0);
+}
+
+// Four values -> four element codes (byte i = value i) under the block's
+// scale code.  The conversion divides by 2^(code - 127), the exponent field
+// of its scale operand, and rounds to nearest even.  Floor mode first clamps
+// each value to +-max_finite * 2^(code - 127) (the saturation the format
+// asks for; ceil mode never exceeds it).
+template <int FMT, int MODE>
+__device__ __forceinline__ uint32_t encode4(const float *y, uint32_t code)
+{
+    const float scale = __uint_as_float(code << 23);
+    if (MODE == MX_FLOOR) {
+        // 1.75 * 2^(code + emax - 127): exponent field code + emax, fraction 0.75
+        const float lim = __uint_as_float(((code + Fp8<FMT>::kEmax) << 23) | 0x600000u);
+        const float a = __builtin_amdgcn_fmed3f(y[0], -lim, lim);
+        const float b = __builtin_amdgcn_fmed3f(y[1], -lim, lim);
+        const float c = __builtin_amdgcn_fmed3f(y[2], -lim, lim);
+        const float d = __builtin_amdgcn_fmed3f(y[3], -lim, lim);
+        return Fp8<FMT>::hi(c, d, scale, Fp8<FMT>::lo(a, b, scale, 0u));
+    }
+    return Fp8<FMT>::hi(y[2], y[3], scale, Fp8<FMT>::lo(y[0], y[1], scale, 0u));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// Largest value over aligned groups of LANES (4 or 8) lanes; every lane of
+// the group ends with it.  All 64 lanes must be active.
+template <int LANES>
+__device__ __forceinline__ uint32_t group_max(uint32_t m)
+{
+    m = max(m, dpp_u<0xB1>(m));       // quad_perm [1,0,3,2]
+    m = max(m, dpp_u<0x4E>(m));       // quad_perm [2,3,0,1]
+    if (LANES == 8)
+        m = max(m, dpp_u<0x141>(m));  // row_half_mirror: lane i <-> 7 - i of each 8
+    return m;
+}
+
+// One lane's vector of E values (vector index v of its row): block maximum,
+// scale, codes.  Codes go to byte offset v * E of the row's code buffer, the
+// scale (from the first lane of the block) to byte v / (32 / E) of the row's
+// scale buffer; both buffers drop stores past their end.
+template <int FMT, int MODE, int E>
+__device__ __forceinline__ void quantize_vector(const float *y, int v, int lane, rsrc_t rc, rsrc_t rs)
+{
+    constexpr int kLanes = kMxBlock / E;
+    const uint32_t m = group_max<kLanes>(lane_amax_bits<E>(y));
+    const uint32_t code = scale_code<FMT, MODE>(m);
+    if (E == 8) {
+        const u32x2 w = {encode4<FMT, MODE>(y, code), encode4<FMT, MODE>(y + 4, code)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, rc, v * 8, 0, kStreaming);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(encode4<FMT, MODE>(y, code), rc, v * 4, 0, kStreaming);
+    }
+    if ((lane & (kLanes - 1)) == 0)
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rs, v / kLanes, 0, kStreaming);
+}
+
+// One value (element paths): code of y under the block's scale code.
+template <int FMT, int MODE>
+__device__ __forceinline__ unsigned char encode1(float y, uint32_t code)
+{
+    const float z[4] = {y, 0.0f, 0.0f, 0.0f};
+    return (unsigned char)(encode4<FMT, MODE>(z, code) & 0xffu);
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Fused forward, 128-bit path (same placement as the bf16 forward).
+template <int IO, bool LB, bool FAST, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+situ_glu_fwd_mx_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
+                           int64_t rw_stride, unsigned char *__restrict__ codes, unsigned char *__restrict__ scales,
+                           int64_t rows, int inter, int waves_per_row, GateK gk, UpK uk)
+{
+    constexpr bool PRECISE = IO == IO_F32;
+    using T = Io<IO>;
+    constexpr int E = T::kPerVec;
+    constexpr int kStrip = 64 * kUnrollMx;
+    const int lane = threadIdx.x & 63;
+    const Place pl = place(waves_per_row);
+    if (pl.row >= rows)
+        return;
+    const int nv = inter / E;
+    const uint32_t half = (uint32_t)nv * 16u;
+    const int nblk = (inter + kMxBlock - 1) / kMxBlock;
+    const int spr = (nv + kStrip - 1) / kStrip;
+    const char *row = static_cast<const char *>(gate_up) + pl.row * (int64_t)half * 2;
+    const rsrc_t rg = make_rsrc(row, half), ru = make_rsrc(row + half, half);
+    const rsrc_t rc = make_rsrc(codes + pl.row * (int64_t)inter, (uint32_t)inter);
+    const rsrc_t rs = make_rsrc(scales + pl.row * (int64_t)nblk, (uint32_t)nblk);
+    const float r = load_rw(rw, rw_bf16, pl.row * rw_stride);
+    const float rscale = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
+    for (int s = pl.strip0; s < spr; s += pl.wpr) {
+        uint4 gv[kUnrollMx], uv[kUnrollMx];
+#pragma unroll
+        for (int k = 0; k < kUnrollMx; ++k) {
+            const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
+            gv[k] = bload(rg, off);
+            uv[k] = bload(ru, off);
+        }
+#pragma unroll
+        for (int k = 0; k < kUnrollMx; ++k) {
+            // past the row end the loads returned zeros: Y = 0 there, which
+            // leaves every block maximum unchanged, and the stores are dropped
+            float g[E], u[E], y[E];
+            T::unpack(gv[k], g);
+            T::unpack(uv[k], u);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                y[e] = fwd_elem<LB, FAST, PRECISE>(g[e], u[e], rscale, gk, uk);
+            quantize_vector<FMT, MODE, E>(y, s * kStrip + 64 * k + lane, lane, rc, rs);
+        }
+    }
+}
+
+// Largest value over each half wavefront (lanes 0-31, 32-63).
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t m)
+{
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    return m;
+}
+
+// Fused forward, element path (any alignment, any intermediate): one
+// wavefront per row, 64 values (two blocks) per step.
+template <int IO, bool LB, bool FAST, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+situ_glu_fwd_mx_elem_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
+                            int64_t rw_stride, unsigned char *__restrict__ codes,
+                            unsigned char *__restrict__ scales, int64_t rows, int inter, int /*unused*/,
+                            GateK gk, UpK uk)
+{
+    constexpr bool PRECISE = IO == IO_F32;
+    using T = Io<IO>;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int nblk = (inter + kMxBlock - 1) / kMxBlock;
+    const float r = load_rw(rw, rw_bf16, row * rw_stride);
+    const float rscale = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
+    const char *gu_row = static_cast<const char *>(gate_up) + row * (int64_t)inter * 2 * T::kBytes;
+    unsigned char *c_row = codes + row * (int64_t)inter;
+    unsigned char *s_row = scales + row * (int64_t)nblk;
+    for (int j0 = 0; j0 < inter; j0 += 64) {
+        const int j = j0 + lane;
+        float y = 0.0f;
+        if (j < inter)
+            y = fwd_elem<LB, FAST, PRECISE>(T::load1(gu_row, j), T::load1(gu_row, (int64_t)inter + j), rscale,
+                                            gk, uk);
+        const uint32_t code = scale_code<FMT, MODE>(half_wave_max(__float_as_uint(y) & 0x7fffffffu));
+        if (j < inter) {
+            c_row[j] = encode1<FMT, MODE>(y, code);
+            if ((lane & 31) == 0)
+                s_row[j / kMxBlock] = (unsigned char)code;
+        }
+    }
+}
+
+// The block quantiser on its own: x [rows, cols] of the io dtype.
+template <int IO, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+situ_glu_mx_quant_vec_kernel(const void *__restrict__ x, unsigned char *__restrict__ codes,
+                             unsigned char *__restrict__ scales, int64_t rows, int cols, int waves_per_row)
+{
+    using T = Io<IO>;
+    constexpr int E = T::kPerVec;
+    constexpr int kStrip = 64 * kUnrollMx;
+    const int lane = threadIdx.x & 63;
+    const Place pl = place(waves_per_row);
+    if (pl.row >= rows)
+        return;
+    const int nv = cols / E;
+    const uint32_t bytes = (uint32_t)nv * 16u;
+    const int nblk = (cols + kMxBlock - 1) / kMxBlock;
+    const int spr = (nv + kStrip - 1) / kStrip;
+    const rsrc_t rx = make_rsrc(static_cast<const char *>(x) + pl.row * (int64_t)bytes, bytes);
+    const rsrc_t rc = make_rsrc(codes + pl.row * (int64_t)cols, (uint32_t)cols);
+    const rsrc_t rs = make_rsrc(scales + pl.row * (int64_t)nblk, (uint32_t)nblk);
+    for (int s = pl.strip0; s < spr; s += pl.wpr) {
+        uint4 xv[kUnrollMx];
+#pragma unroll
+        for (int k = 0; k < kUnrollMx; ++k)
+            xv[k] = bload(rx, (uint32_t)(s * kStrip + 64 * k + lane) * 16u);
+#pragma unroll
+        for (int k = 0; k < kUnrollMx; ++k) {
+            float y[E];
+            T::unpack(xv[k], y);
+            quantize_vector<FMT, MODE, E>(y, s * kStrip + 64 * k + lane, lane, rc, rs);
+        }
+    }
+}
+
+template <int IO, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+situ_glu_mx_quant_elem_kernel(const void *__restrict__ x, unsigned char *__restrict__ codes,
+                              unsigned char *__restrict__ scales, int64_t rows, int cols, int /*unused*/)
+{
+    using T = Io<IO>;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int nblk = (cols + kMxBlock - 1) / kMxBlock;
+    const char *x_row = static_cast<const char *>(x) + row * (int64_t)cols * T::kBytes;
+    unsigned char *c_row = codes + row * (int64_t)cols;
+    unsigned char *s_row = scales + row * (int64_t)nblk;
+    for (int j0 = 0; j0 < cols; j0 += 64) {
+        const int j = j0 + lane;
+        const float y = j < cols ? T::load1(x_row, j) : 0.0f;
+        const uint32_t code = scale_code<FMT, MODE>(half_wave_max(__float_as_uint(y) & 0x7fffffffu));
+        if (j < cols) {
+            c_row[j] = encode1<FMT, MODE>(y, code);
+            if ((lane & 31) == 0)
+                s_row[j / kMxBlock] = (unsigned char)code;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+using FwdMxFn = void (*)(const void *, const void *, int, int64_t, unsigned char *, unsigned char *, int64_t, int,
+                         int, GateK, UpK);
+using QuantFn = void (*)(const void *, unsigned char *, unsigned char *, int64_t, int, int);
+
+template <int IO, bool VEC, bool LB, bool FAST, int FMT, int MODE>
+constexpr FwdMxFn fwd_mx_fn()
+{
+    if constexpr (VEC)
+        return situ_glu_fwd_mx_vec_kernel<IO, LB, FAST, FMT, MODE>;
+    else
+        return situ_glu_fwd_mx_elem_kernel<IO, LB, FAST, FMT, MODE>;
+}
+template <int IO, bool VEC, int FMT, int MODE>
+constexpr QuantFn quant_fn()
+{
+    if constexpr (VEC)
+        return situ_glu_mx_quant_vec_kernel<IO, FMT, MODE>;
+    else
+        return situ_glu_mx_quant_elem_kernel<IO, FMT, MODE>;
+}
+
+#define SITU_MX_FM(IO, VEC, LB, FAST, FMT) {fwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_FLOOR>(), fwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_CEIL>()}
+#define SITU_MX_CASE(IO, VEC, LB, FAST) {SITU_MX_FM(IO, VEC, LB, FAST, FP8_E4M3), SITU_MX_FM(IO, VEC, LB, FAST, FP8_E5M2)}
+#define SITU_MX_ROW(IO, VEC)                                                                         \
+    { SITU_MX_CASE(IO, VEC, false, false), SITU_MX_CASE(IO, VEC, false, true),                      \
+      SITU_MX_CASE(IO, VEC, true, false), SITU_MX_CASE(IO, VEC, true, true) }
+// index: [io][vec][lb * 2 + fast][fmt][mode]
+const FwdMxFn kFwdMx[2][2][4][2][2] = {
+    {SITU_MX_ROW(IO_F32, false), SITU_MX_ROW(IO_F32, true)},
+    {SITU_MX_ROW(IO_BF16, false), SITU_MX_ROW(IO_BF16, true)},
+};
+#define SITU_Q_FM(IO, VEC, FMT) {quant_fn<IO, VEC, FMT, MX_FLOOR>(), quant_fn<IO, VEC, FMT, MX_CEIL>()}
+// index: [io][vec][fmt][mode]
+const QuantFn kQuant[2][2][2][2] = {
+    {{SITU_Q_FM(IO_F32, false, FP8_E4M3), SITU_Q_FM(IO_F32, false, FP8_E5M2)},
+     {SITU_Q_FM(IO_F32, true, FP8_E4M3), SITU_Q_FM(IO_F32, true, FP8_E5M2)}},
+    {{SITU_Q_FM(IO_BF16, false, FP8_E4M3), SITU_Q_FM(IO_BF16, false, FP8_E5M2)},
+     {SITU_Q_FM(IO_BF16, true, FP8_E4M3), SITU_Q_FM(IO_BF16, true, FP8_E5M2)}},
+};
+
+}  // namespace
+
+int launch_fwd_mx(const FwdMxLaunch &L, void *stream)
+{
+    const Shape sh = shape(L.rows, L.inter, L.io, L.vec, L.rows_per_block, kUnrollMx);
+    const FwdMxFn fn = kFwdMx[L.io][L.vec][L.lb * 2 + L.fast][L.fmt][L.ceil_mode ? MX_CEIL : MX_FLOOR];
+    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up, L.rw, L.rw_bf16, L.rw_stride,
+                       static_cast<unsigned char *>(L.codes), static_cast<unsigned char *>(L.scales), L.rows,
+                       L.inter, sh.waves_per_row, L.gk, L.uk);
+    return (int)hipGetLastError();
+}
+
+int launch_mx_quant(const MxQuantLaunch &L, void *stream)
+{
+    const Shape sh = shape(L.rows, L.cols, L.io, L.vec, L.rows_per_block, kUnrollMx);
+    const QuantFn fn = kQuant[L.io][L.vec][L.fmt][L.ceil_mode ? MX_CEIL : MX_FLOOR];
+    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.x, static_cast<unsigned char *>(L.codes),
+                       static_cast<unsigned char *>(L.scales), L.rows, L.cols, sh.waves_per_row);
+    return (int)hipGetLastError();
+}
+
+}  // namespace situ

@@ -127,6 +127,76 @@ def situ_glu_bwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, grad_out:
     return d_gate_up, d_routing_weights
 
 
+_FP8 = {"e4m3": _capi.SITU_FP8_E4M3, "e5m2": _capi.SITU_FP8_E5M2}
+_MODES = {"floor": _capi.SITU_MX_SCALE_FLOOR, "ceil": _capi.SITU_MX_SCALE_CEIL}
+
+
+def _mx_args(fp8_format: str, scale_mode: str):
+    try:
+        return _FP8[fp8_format], _MODES[scale_mode]
+    except KeyError:
+        raise ValueError(f"fp8_format must be one of {sorted(_FP8)} and scale_mode one of {sorted(_MODES)}, "
+                         f"got {fp8_format!r}, {scale_mode!r}") from None
+
+
+def _mx_outputs(lead, cols, device, codes, scales):
+    nblk = -(-cols // _capi.SITU_MX_BLOCK)
+    if codes is None:
+        codes = torch.empty(lead + (cols,), dtype=torch.uint8, device=device)
+    elif codes.dtype != torch.uint8 or tuple(codes.shape) != lead + (cols,) or not codes.is_contiguous():
+        raise ValueError(f"codes must be a contiguous uint8 tensor of shape {lead + (cols,)}")
+    if scales is None:
+        scales = torch.empty(lead + (nblk,), dtype=torch.uint8, device=device)
+    elif scales.dtype != torch.uint8 or tuple(scales.shape) != lead + (nblk,) or not scales.is_contiguous():
+        raise ValueError(f"scales must be a contiguous uint8 tensor of shape {lead + (nblk,)}")
+    return codes, scales
+
+
+def situ_glu_fwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, beta: float = 4.0,
+                       linear_beta: float | None = 25.0, fp8_format: str = "e4m3", scale_mode: str = "floor",
+                       codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Forward with MXFP8 output: returns (codes uint8 [..., I], scales uint8
+    [..., ceil(I / 32)]), blocks of 32 along the last axis with E8M0 scales.
+
+    ``codes.view(torch.float8_e4m3fn)`` (or ``float8_e5m2``) gives the
+    elements; the value of element j is element * 2^(scales[..., j // 32] - 127).
+    """
+    lib = _capi.load()
+    _check_device(gate_up, routing_weights, codes, scales)
+    io = _io_dtype(gate_up, "gate_up")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    fmt, mode = _mx_args(fp8_format, scale_mode)
+    lead, rows, inter, rw_rows = _flatten(gate_up, routing_weights)
+    codes, scales = _mx_outputs(lead, inter, gate_up.device, codes, scales)
+    _capi.check(lib.situ_glu_fwd_mxfp8(gate_up.data_ptr(), io, rows, inter, routing_weights.data_ptr(), rwd,
+                                       rw_rows, float(beta), _capi.lb_ptr(linear_beta), fmt, mode,
+                                       codes.data_ptr(), scales.data_ptr(), _stream()), lib)
+    return codes, scales
+
+
+def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: str = "floor",
+                         codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """MXFP8 block quantisation of x [..., cols] (float32 or bfloat16) along its
+    last axis: returns (codes uint8 [..., cols], scales uint8 [..., ceil(cols / 32)])."""
+    lib = _capi.load()
+    _check_device(x, codes, scales)
+    io = _io_dtype(x, "x")
+    fmt, mode = _mx_args(fp8_format, scale_mode)
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous tensor with at least one dimension")
+    lead = tuple(x.shape[:-1])
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if cols == 0:
+        rows = 1
+        for d in lead:
+            rows *= d
+    codes, scales = _mx_outputs(lead, cols, x.device, codes, scales)
+    _capi.check(lib.situ_glu_mx_quantize(x.data_ptr(), io, rows, cols, fmt, mode, codes.data_ptr(),
+                                         scales.data_ptr(), _stream()), lib)
+    return codes, scales
+
+
 def situ_glu_last_error() -> str:
     return _capi.last_error()
 

@@ -30,6 +30,10 @@ torch's round-to-nearest-even; "N(0, s)" means s * randn):
                 sigmoid); routing weights [131072, 1] ~ U(0, 1); grad_out bf16
                 ~ N(0, 1); beta 4, linear_beta 25; forward + backward with
                 d_routing_weights; rows in natural order.
+  routed_top8_mxfp8
+                the routed_top8 inputs (same draws), forward only, with the
+                output written as MXFP8 (E4M3 elements, 32-value blocks,
+                floor scale rule) instead of bf16.
 """
 from __future__ import annotations
 
@@ -50,6 +54,8 @@ class Workload:
     want_drw: bool
     broadcast_rw: bool
     description: str
+    recipe: str | None = None      # draw the inputs of this workload instead (same seed, same order)
+    mx: str | None = None          # forward output as MXFP8 with this element format
 
 
 WORKLOADS = {
@@ -66,8 +72,11 @@ WORKLOADS = {
     "stress_sat": Workload("stress_sat", 131072, 2048, torch.bfloat16, 4.0, 25.0, True, True, False,
                            "bf16 gate_up [131072, 2*2048] N(0,8) with 5% at +-U(30,60), "
                            "r ~ U(0,1), fwd+bwd+dr"),
+    "routed_top8_mxfp8": Workload("routed_top8_mxfp8", 65536, 2048, torch.bfloat16, 4.0, 25.0, False, False,
+                                  False, "routed_top8 inputs, forward only, output MXFP8 (E4M3, blocks of 32, "
+                                  "E8M0 floor scales)", recipe="routed_top8", mx="e4m3"),
 }
-ORDER = ["fp32_small", "top1_fwd", "dense_ffn", "routed_top8", "stress_sat"]
+ORDER = ["fp32_small", "top1_fwd", "dense_ffn", "routed_top8", "stress_sat", "routed_top8_mxfp8"]
 
 
 def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
@@ -76,6 +85,10 @@ def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
     smaller or ragged instance of the same recipe; for routed_top8 rows must be
     a multiple of 8)."""
     w = WORKLOADS[name]
+    if w.recipe is not None:
+        x = make_inputs(w.recipe, device, seed, rows, inter)
+        x.update(workload=w, grad_out=None, want_drw=False)
+        return x
     rows = w.rows if rows is None else int(rows)
     if inter is not None:
         from dataclasses import replace
@@ -128,14 +141,16 @@ def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
 def algorithmic_bytes(name: str, rows: int | None = None) -> dict:
     """Bytes the method must move: read every input once, write every output once.
 
-    forward : gate_up + routing weights + out
+    forward : gate_up + routing weights + out (MXFP8 output: one byte per
+              value plus one scale byte per 32-value block)
     backward: gate_up + routing weights + grad_out + d_gate_up (+ d_routing_weights)
     """
     w = WORKLOADS[name]
     rows = w.rows if rows is None else rows
     s = torch.finfo(w.dtype).bits // 8
     rw_bytes = 4 * (1 if w.broadcast_rw else rows)
-    fwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s
+    out_bytes = rows * (w.inter + -(-w.inter // 32)) if w.mx else rows * w.inter * s
+    fwd = rows * 2 * w.inter * s + rw_bytes + out_bytes
     bwd = 0
     if w.backward:
         bwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s + rows * 2 * w.inter * s

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 1
+#define SITU_GLU_ABI_VERSION 2
 
 /* return codes */
 #define SITU_OK 0
@@ -71,6 +71,15 @@ extern "C" {
 /* element types */
 #define SITU_DTYPE_F32 0
 #define SITU_DTYPE_BF16 1
+
+/* MXFP8 element formats (OCP 8-bit floating point: E4M3 with bias 7, no
+ * infinities, largest 448; E5M2 with bias 15, largest 57344) and scale modes
+ * (OCP Microscaling Formats (MX) v1.0, see situ_glu_fwd_mxfp8) */
+#define SITU_FP8_E4M3 0
+#define SITU_FP8_E5M2 1
+#define SITU_MX_SCALE_FLOOR 0   /* s = floor(log2(amax)) - emax_elem (the MX rule) */
+#define SITU_MX_SCALE_CEIL 1    /* smallest s with amax <= max_finite * 2^s */
+#define SITU_MX_BLOCK 32        /* values per scale, along each row */
 
 /*
  * Forward: out = r * T_g(G) * T_u(U).
@@ -140,6 +149,66 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows,
  */
 size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate,
                                     int64_t rw_rows);
+
+/*
+ * Forward with MXFP8 output: Y = r * T_g(G) * T_u(U) as in situ_glu_fwd,
+ * written as MXFP8 blocks instead of io_dtype values.  The Megatron-LM PR
+ * "[Dev] Add SiTU-GLU through Transformer Engine" (section "Validation") runs
+ * the activation under MXFP8 block scaling; the format is the OCP
+ * Microscaling Formats (MX) v1.0 one:
+ *   - each row of Y is cut into blocks of SITU_MX_BLOCK (32) consecutive
+ *     values, the last block of a row holding intermediate % 32 values when
+ *     that is not 0;
+ *   - each block has one E8M0 scale X = 2^s, stored as the byte s + 127;
+ *     SITU_MX_SCALE_FLOOR: s = floor(log2(amax)) - emax_elem (emax_elem = 8
+ *     for E4M3, 15 for E5M2), where amax is the block's largest |Y|;
+ *     SITU_MX_SCALE_CEIL: the smallest s with amax <= max_finite * 2^s (no
+ *     element saturates); s is clamped to [-127, 127], so an all-zero block
+ *     gets the byte 0;
+ *   - each value is stored as the element code nearest Y / X (ties to the
+ *     even code), magnitudes past the largest finite value clamped to it;
+ *   - a block holding a NaN or an infinity gets the scale byte 255 (NaN); its
+ *     element bytes are unspecified.
+ * Y is computed in fp32 as for situ_glu_fwd; the rounding to the element
+ * format is the only rounding after it.
+ *
+ *   gate_up ... linear_beta  as for situ_glu_fwd
+ *   fp8_format       SITU_FP8_E4M3 or SITU_FP8_E5M2
+ *   scale_mode       SITU_MX_SCALE_FLOOR or SITU_MX_SCALE_CEIL
+ *   codes            device pointer, [rows, intermediate] bytes (row major)
+ *   scales           device pointer, [rows, ceil(intermediate / 32)] bytes
+ *   stream           hipStream_t or NULL
+ * codes and scales must not overlap the inputs or each other.  Any pointer
+ * alignment is accepted; a 16-byte-aligned gate_up with intermediate a
+ * multiple of 8 (bf16) or 4 (fp32) and codes aligned to 8 (bf16) or 4 (fp32)
+ * bytes take the 128-bit path.  Returns as situ_glu_fwd; an unknown format or
+ * mode is SITU_ERR_INVALID_ARG.
+ */
+int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows,
+                       int64_t intermediate, const void *routing_weights,
+                       int rw_dtype, int64_t rw_rows, double beta,
+                       const double *linear_beta, int fp8_format,
+                       int scale_mode, void *codes, void *scales,
+                       void *stream);
+
+/*
+ * The MXFP8 block quantiser of situ_glu_fwd_mxfp8 on its own: x [rows, cols]
+ * (io_dtype, row major, device memory) becomes codes [rows, cols] bytes and
+ * scales [rows, ceil(cols / 32)] bytes, with the blocks, scale modes and
+ * rounding described above, by the same device code.  For callers that hold
+ * Y (or any other activation) in fp32 or bf16.
+ *   x                device pointer, [rows, cols] of io_dtype
+ *   io_dtype         SITU_DTYPE_F32 or SITU_DTYPE_BF16
+ *   rows, cols       >= 0 (cols <= 2^30 - 1, rows <= 2^31 - 1)
+ *   fp8_format, scale_mode, codes, scales, stream   as for situ_glu_fwd_mxfp8
+ * Returns SITU_OK, SITU_ERR_INVALID_ARG (bad dtype, format, mode, NULL
+ * pointer, negative size, overlapping buffers), SITU_ERR_UNSUPPORTED (too
+ * large) or SITU_ERR_DEVICE (launch failed).  rows == 0 or cols == 0 is a
+ * valid empty call.
+ */
+int situ_glu_mx_quantize(const void *x, int io_dtype, int64_t rows,
+                         int64_t cols, int fp8_format, int scale_mode,
+                         void *codes, void *scales, void *stream);
 
 /* Message describing the last error on the calling thread ("" if none). */
 const char *situ_glu_last_error(void);

@@ -83,6 +83,12 @@ def _bind(lib):
     lib.mx_oracle_quantize_block.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p, u8p]
     lib.mx_oracle_quantize_rows.restype = None
     lib.mx_oracle_quantize_rows.argtypes = [i64, i64, _dp, ctypes.c_int, ctypes.c_int, u8p, u8p]
+    lib.mx_oracle_fp8_encode_array.restype = None
+    lib.mx_oracle_fp8_encode_array.argtypes = [i64, _dp, ctypes.c_int, u8p]
+    lib.mx_oracle_fp8_decode_array.restype = None
+    lib.mx_oracle_fp8_decode_array.argtypes = [i64, u8p, ctypes.c_int, _dp]
+    lib.mx_oracle_scale_code_array.restype = None
+    lib.mx_oracle_scale_code_array.argtypes = [i64, _dp, ctypes.c_int, ctypes.c_int, u8p]
     return lib
 
 
@@ -286,3 +292,30 @@ def mx_quantize(x, fmt="e4m3", mode="floor", threads: int = 1, lib=None):
 
     _run_blocks(run, rows, threads)
     return codes, scales
+
+
+def fp8_encode_array(x, fmt="e4m3", lib=None) -> np.ndarray:
+    """fp8_encode over an array (uint8 codes, same shape)."""
+    lib = lib or load()
+    a = _as_f64(x)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib.mx_oracle_fp8_encode_array(a.size, _ptr(a), _fmt(fmt), _ptr(out, ctypes.c_uint8))
+    return out
+
+
+def fp8_decode_array(codes, fmt="e4m3", lib=None) -> np.ndarray:
+    """fp8_decode over an array of codes (float64, same shape)."""
+    lib = lib or load()
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.mx_oracle_fp8_decode_array(c.size, _ptr(c, ctypes.c_uint8), _fmt(fmt), _ptr(out))
+    return out
+
+
+def mx_scale_code_array(amax, fmt="e4m3", mode="floor", lib=None) -> np.ndarray:
+    """mx_scale_code over an array of block maxima (uint8 codes)."""
+    lib = lib or load()
+    a = _as_f64(amax)
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib.mx_oracle_scale_code_array(a.size, _ptr(a), _fmt(fmt), _mode(mode), _ptr(out, ctypes.c_uint8))
+    return out

@@ -181,3 +181,23 @@ void mx_oracle_quantize_rows(int64_t rows, int64_t cols, const double *x, int fm
                                      scales + i * nblk + b);
         }
 }
+
+/* Element-wise array forms of the functions above (used by the tests to
+ * bound what a GPU code may be). */
+void mx_oracle_fp8_encode_array(int64_t n, const double *x, int fmt, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = mx_oracle_fp8_encode(x[i], fmt);
+}
+
+void mx_oracle_fp8_decode_array(int64_t n, const uint8_t *codes, int fmt, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = mx_oracle_fp8_decode(codes[i], fmt);
+}
+
+void mx_oracle_scale_code_array(int64_t n, const double *amax, int fmt, int mode, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (uint8_t)mx_oracle_scale_code(amax[i], fmt, mode);
+}

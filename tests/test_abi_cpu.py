@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == 1
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 2
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -107,6 +107,62 @@ def test_bwd_rejects(lib, capi, kw):
     assert capi.last_error(lib) != ""
 
 
+def _fwd_mx(lib, **kw):
+    a = dict(gate_up=FAKE, io=1, rows=4, inter=40, rw=FAKE + 4096, rwd=0, rw_rows=4, beta=4.0, lb=25.0,
+             fmt=0, mode=0, codes=FAKE + 8192, scales=FAKE + 16384)
+    a.update(kw)
+    lb = None if a["lb"] is None else ctypes.pointer(ctypes.c_double(a["lb"]))
+    return lib.situ_glu_fwd_mxfp8(a["gate_up"], a["io"], a["rows"], a["inter"], a["rw"], a["rwd"],
+                                  a["rw_rows"], a["beta"], lb, a["fmt"], a["mode"], a["codes"], a["scales"],
+                                  None)
+
+
+def _quant(lib, **kw):
+    a = dict(x=FAKE, io=0, rows=4, cols=40, fmt=0, mode=0, codes=FAKE + 8192, scales=FAKE + 16384)
+    a.update(kw)
+    return lib.situ_glu_mx_quantize(a["x"], a["io"], a["rows"], a["cols"], a["fmt"], a["mode"], a["codes"],
+                                    a["scales"], None)
+
+
+# codes: 4 x 40 bytes at FAKE + 8192; scales: 4 x 2 bytes at FAKE + 16384
+BAD_FWD_MX = [
+    dict(io=2), dict(beta=0.0), dict(lb=-1.0), dict(rw_rows=2), dict(fmt=2), dict(fmt=-1), dict(mode=2),
+    dict(codes=None), dict(scales=None), dict(gate_up=None),
+    dict(codes=FAKE + 100),                          # overlaps gate_up (4 x 80 x 2 bytes)
+    dict(scales=FAKE + 4096 + 2),                    # overlaps routing weights
+    dict(scales=FAKE + 8192 + 150),                  # overlaps codes
+]
+BAD_QUANT = [
+    dict(io=5), dict(fmt=3), dict(mode=-1), dict(rows=-1), dict(cols=-1), dict(x=None), dict(codes=None),
+    dict(scales=None), dict(x=FAKE + 2),             # fp32 x must be 4-byte aligned
+    dict(codes=FAKE + 600),                          # overlaps x (4 x 40 x 4 bytes)
+    dict(scales=FAKE + 8192 + 159),                  # overlaps codes
+]
+
+
+@pytest.mark.parametrize("kw", BAD_FWD_MX, ids=[str(k) for k in BAD_FWD_MX])
+def test_fwd_mxfp8_rejects(lib, capi, kw):
+    assert _fwd_mx(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
+    assert capi.last_error(lib) != ""
+
+
+@pytest.mark.parametrize("kw", BAD_QUANT, ids=[str(k) for k in BAD_QUANT])
+def test_mx_quantize_rejects(lib, capi, kw):
+    assert _quant(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
+    assert capi.last_error(lib) != ""
+
+
+def test_mx_empty_and_unsupported(lib, capi):
+    # empty calls succeed without touching any pointer
+    assert _fwd_mx(lib, rows=0, rw_rows=0, codes=None, scales=None) == capi.SITU_OK
+    assert _fwd_mx(lib, inter=0, codes=None, scales=None) == capi.SITU_OK
+    assert _quant(lib, rows=0, x=None, codes=None, scales=None) == capi.SITU_OK
+    assert _quant(lib, cols=0, x=None, codes=None, scales=None) == capi.SITU_OK
+    assert _quant(lib, cols=1 << 30, rows=1) == capi.SITU_ERR_UNSUPPORTED
+    assert _quant(lib, rows=1 << 31) == capi.SITU_ERR_UNSUPPORTED
+    assert _fwd_mx(lib, inter=1 << 30, rows=1, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+
+
 def test_unsupported_sizes(lib, capi):
     assert _fwd(lib, inter=1 << 30, rows=1, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
     assert _fwd(lib, rows=1 << 31, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
@@ -166,6 +222,16 @@ def test_gate_window_constants(capi, lib):
             tol = 1e-4 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d))
             assert abs(p2 - t) <= tol, (beta, d, p2, t)
     assert lib.situ_glu_gate_window(-1.0, out) == capi.SITU_ERR_INVALID_ARG
+
+
+def test_mx_python_layer_rejects():
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_fwd_mxfp8, situ_glu_mx_quantize
+    with pytest.raises(ValueError):
+        situ_glu_fwd_mxfp8(torch.zeros(2, 64), torch.ones(2, 1))
+    with pytest.raises(ValueError):
+        situ_glu_mx_quantize(torch.zeros(2, 64))
 
 
 def test_autograd_rejects_cpu_tensors():
