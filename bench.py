@@ -6,15 +6,16 @@
 One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
 inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
-forward with MXFP8 output instead (forward only).  W untimed steps, then K timed steps between
-two device synchronisations.  Prints ONE JSON line:
+forward with MXFP8 output instead (forward only).  W untimed steps, then K
+timed steps between two device synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
                the method must move (every input read once, every output
                written once) / wall time per step
   roofline     the dominant kernel (the backward) against the MI355X HBM peak
                (8 TB/s): algorithmic bytes per launch / its mean launch time,
-               timed with HIP events on the stream it runs on
+               timed with HIP events on the stream it runs on around K
+               back-to-back launches of that kernel
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
                (a reported baseline, not the target)
 
@@ -99,7 +100,9 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks take ~50 steps (~25 ms) to settle from idle; 200 warm-up
+    # steps keep that ramp out of the timed region
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="routed_top8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=65536,
@@ -136,19 +139,19 @@ def main(argv=None) -> int:
     drw = torch.empty_like(rw) if want else None
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def fwd():
         if w.mx:
             situ_glu_fwd_mxfp8(gu, rw, beta, lb, w.mx, "floor", codes=codes, scales=scales)
         else:
             situ_glu_fwd(gu, rw, beta, lb, out=y)
-        if ev is not None:
-            ev[1].record()
+
+    def bwd():
+        situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
+
+    def step():
+        fwd()
         if w.backward:
-            situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
-        if ev is not None:
-            ev[2].record()
+            bwd()
 
     for _ in range(args.warmup):
         step()
@@ -160,14 +163,21 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # ... and the same K steps again with HIP events around each kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ... then each kernel on its own: K back-to-back launches between two HIP
+    # events on the launch stream (the launches are independent of each other)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
-    for e in evs:
-        step(e)
+    ev[0].record()
+    for _ in range(args.steps):
+        fwd()
+    ev[1].record()
+    if w.backward:
+        for _ in range(args.steps):
+            bwd()
+    ev[2].record()
     torch.cuda.synchronize()
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if w.backward else 0.0
+    fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / args.steps if w.backward else 0.0
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
