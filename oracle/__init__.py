@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
 leg of ``bench.py`` may import this package; the product path never does.  The
-arithmetic lives in ``situ_oracle.c`` (the activation and its gradients) and
-``mx_oracle.c`` (MXFP8 block quantisation), plain C in double precision with
-libm, sharing nothing with the HIP library.  This module only compiles them
+arithmetic lives in ``situ_oracle.c`` (the activation and its gradients),
+``mx_oracle.c`` (MXFP8 block quantisation) and ``attn_res_oracle.c``
+(attention-residual mixing), plain C in double precision with libm, sharing
+nothing with the HIP library.  This module only compiles them
 with gcc, loads them with ctypes and marshals numpy arrays.
 
 Definitions followed (see the header of ``situ_oracle.c``):
@@ -32,6 +33,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "situ_oracle.c")
 _MX_SRC = os.path.join(_HERE, "mx_oracle.c")
+_ARES_SRC = os.path.join(_HERE, "attn_res_oracle.c")
 _LIB = os.path.join(_HERE, "libsitu_oracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -39,11 +41,11 @@ _lib = None
 _dp = ctypes.POINTER(ctypes.c_double)
 
 
-def build(src: str = _SRC, out: str = _LIB, mx_src: str = _MX_SRC) -> str:
+def build(src: str = _SRC, out: str = _LIB, mx_src: str = _MX_SRC, ares_src: str = _ARES_SRC) -> str:
     """Compile the oracle with gcc (no fast-math: IEEE double semantics)."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, mx_src, "-lm"]
+           "-ffp-contract=off", "-Wall", "-Wextra", "-o", tmp, src, mx_src, ares_src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -89,6 +91,9 @@ def _bind(lib):
     lib.mx_oracle_fp8_decode_array.argtypes = [i64, u8p, ctypes.c_int, _dp]
     lib.mx_oracle_scale_code_array.restype = None
     lib.mx_oracle_scale_code_array.argtypes = [i64, _dp, ctypes.c_int, ctypes.c_int, u8p]
+    lib.ares_oracle_forward.restype = None
+    lib.ares_oracle_forward.argtypes = [i64, i64, ctypes.c_int, i64, _dp, _dp, _dp, _dp, ctypes.c_double,
+                                        _dp, _dp, _dp, _dp, _dp]
     return lib
 
 
@@ -319,3 +324,38 @@ def mx_scale_code_array(amax, fmt="e4m3", mode="floor", lib=None) -> np.ndarray:
     out = np.empty(a.shape, dtype=np.uint8)
     lib.mx_oracle_scale_code_array(a.size, _ptr(a), _fmt(fmt), _mode(mode), _ptr(out, ctypes.c_uint8))
     return out
+
+
+# ----------------------------------------------------------------- attention-residual mixing
+
+ARES_MAX_BLOCKS = 64
+
+
+def attn_res_forward(blocks, prefix, norm_w, proj_w, eps: float, threads: int = 1, lib=None) -> dict:
+    """fp64 attention-residual mixing.
+
+    blocks [T, m, H]; prefix [T, H] or None (values = blocks followed by the
+    prefix along the block axis).  Returns out [T, H], logits / probs /
+    absdot [T, NB] and scale [T, H] (see attn_res_oracle.c)."""
+    lib = lib or load()
+    bl = _as_f64(blocks)
+    T, m, H = bl.shape
+    has = prefix is not None
+    pf = _as_f64(prefix).reshape(T, H) if has else np.zeros((max(T, 1), max(H, 1)))
+    nb = m + (1 if has else 0)
+    assert 1 <= nb <= ARES_MAX_BLOCKS
+    w = _as_f64(norm_w).reshape(H)
+    p = _as_f64(proj_w).reshape(H)
+    out = np.empty((T, H))
+    logits = np.empty((T, nb))
+    probs = np.empty((T, nb))
+    absdot = np.empty((T, nb))
+    scale = np.empty((T, H))
+
+    def run(lo, hi):
+        lib.ares_oracle_forward(hi - lo, m, int(has), H, _ptr(bl[lo:hi]), _ptr(pf[lo:hi] if has else pf),
+                                _ptr(w), _ptr(p), float(eps), _ptr(out[lo:hi]), _ptr(logits[lo:hi]),
+                                _ptr(probs[lo:hi]), _ptr(absdot[lo:hi]), _ptr(scale[lo:hi]))
+
+    _run_blocks(run, T, threads)
+    return {"out": out, "logits": logits, "probs": probs, "absdot": absdot, "scale": scale}

@@ -112,3 +112,31 @@ def mx_blocks():
                     c = [int(t, 16) for t in toks]
                     cur["codes"] = c + [0] * (cur["cols"] - len(c))
     return out
+
+
+def attn_res_cases():
+    """Hand-worked attention-residual cases (tests/golden/attn_res_cases.txt)."""
+    out = []
+    cur = None
+    with open(os.path.join(GOLDEN, "attn_res_cases.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *toks = line.split()
+            if key == "case":
+                cur = {"name": toks[0], "blocks": [], "prefix": None}
+                out.append(cur)
+            elif key == "H":
+                cur["H"] = int(toks[0])
+            elif key == "eps":
+                cur["eps"] = float(Fraction(toks[0]))
+            elif key in ("w", "p"):
+                cur[key] = [parse_x(t) for t in toks]
+            elif key == "block":
+                cur["blocks"].append([float(Fraction(t)) for t in toks])
+            elif key == "prefix":
+                cur["prefix"] = [float(Fraction(t)) for t in toks]
+            elif key in ("probs", "out"):
+                cur[key] = [Fraction(t) for t in toks]
+    return out

@@ -11,6 +11,9 @@ AssertionError when the oracle disagrees with:
   * central finite differences of the oracle's own forward,
   * the exact linearity of Y in the routing weight,
   * bfloat16 / fp32 rounding by torch and numpy,
+  * attention-residual mixing: hand-worked cases
+    (tests/golden/attn_res_cases.txt), the same chain composed of torch's
+    library routines (rms_norm, matmul, softmax), and its invariants,
   * MXFP8: hand-worked blocks (tests/golden/mx_blocks.txt), torch's own
     float8_e4m3fn / float8_e5m2 codecs, numpy's binary16 (whose top byte is
     E5M2), exact rational rounding with Python's fractions, and the bounds
@@ -25,7 +28,7 @@ import math
 import numpy as np
 
 import oracle
-from golden_io import closed_forms, mx_blocks, worked_cases
+from golden_io import attn_res_cases, closed_forms, mx_blocks, worked_cases
 
 # tribonacci constant: real root of t^3 = t^2 + t + 1 (Cardano)
 _TRIB = (1.0 + (19.0 + 3.0 * math.sqrt(33.0)) ** (1.0 / 3.0)
@@ -535,6 +538,96 @@ def pin_mx_block_properties(lib):
                     e = max(math.floor(math.log2(abs(v))) if v else 0, 1 - p["bias"])
                     q = 2.0 ** (e - p["mbits"])
                     assert abs(d - v) <= q / 2, (fmt, mode, i, j, v, d)
+
+
+# --------------------------------------------------------------------------
+# attention-residual mixing
+# --------------------------------------------------------------------------
+
+def pin_ares_golden(lib):
+    for c in attn_res_cases():
+        H = c["H"]
+        blocks = np.array(c["blocks"], dtype=np.float64).reshape(1, -1, H)
+        prefix = None if c["prefix"] is None else np.array(c["prefix"]).reshape(1, H)
+        r = oracle.attn_res_forward(blocks, prefix, c["w"], c["p"], c["eps"], lib=lib)
+        for got, want in zip(r["probs"][0], c["probs"]):
+            _close(got, float(want), 1e-14, 1e-15, f"{c['name']} probs")
+        for got, want in zip(r["out"][0], c["out"]):
+            _close(got, float(want), 1e-14, 1e-14, f"{c['name']} out")
+
+
+def _ares_library(blocks, prefix, w, p, eps):
+    """The chain composed of torch library routines (float64)."""
+    import torch
+    v = torch.from_numpy(blocks)
+    if prefix is not None:
+        v = torch.cat([v, torch.from_numpy(prefix).unsqueeze(1)], dim=1)
+    n = torch.nn.functional.rms_norm(v, (v.shape[-1],), weight=torch.from_numpy(np.asarray(w, np.float64)),
+                                     eps=eps)
+    logits = torch.matmul(n, torch.from_numpy(np.asarray(p, np.float64)))
+    prob = torch.softmax(logits, dim=1)
+    out = torch.matmul(prob.unsqueeze(1), v).squeeze(1)
+    return out.numpy(), prob.numpy()
+
+
+def pin_ares_vs_library(lib):
+    rng = np.random.default_rng(41)
+    for T, m, H, pref, eps in ((5, 3, 64, True, 1e-6), (4, 8, 200, True, 1e-2), (3, 2, 33, False, 0.5),
+                               (2, 1, 16, False, 1e-6)):
+        blocks = rng.normal(0, 1, (T, m, H)) * np.exp(rng.uniform(-2, 2, (T, m, 1)))
+        prefix = rng.normal(0, 3, (T, H)) if pref else None
+        w = 1 + 0.3 * rng.normal(0, 1, H)
+        p = rng.normal(0, 2 / np.sqrt(H), H)
+        r = oracle.attn_res_forward(blocks, prefix, w, p, eps, lib=lib)
+        out, prob = _ares_library(blocks, prefix, w, p, eps)
+        np.testing.assert_allclose(r["probs"], prob, rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(r["out"], out, rtol=1e-11, atol=1e-12 * np.abs(out).max())
+
+
+def pin_ares_invariants(lib):
+    rng = np.random.default_rng(43)
+    T, m, H = 3, 4, 24
+    blocks = rng.normal(0, 1, (T, m, H))
+    prefix = rng.normal(0, 1, (T, H))
+    w = 1 + 0.2 * rng.normal(0, 1, H)
+    p = rng.normal(0, 0.5, H)
+    base = oracle.attn_res_forward(blocks, prefix, w, p, 1e-3, lib=lib)
+    # the prefix is the last block: split and stacked forms agree
+    stacked = np.concatenate([blocks, prefix[:, None, :]], axis=1)
+    st = oracle.attn_res_forward(stacked, None, w, p, 1e-3, lib=lib)
+    np.testing.assert_allclose(st["out"], base["out"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(st["probs"], base["probs"], rtol=1e-14)
+    # permuting the blocks permutes the probabilities and leaves out unchanged
+    perm = [2, 4, 0, 3, 1]
+    pm = oracle.attn_res_forward(stacked[:, perm], None, w, p, 1e-3, lib=lib)
+    np.testing.assert_allclose(pm["probs"], base["probs"][:, perm], rtol=1e-13)
+    np.testing.assert_allclose(pm["out"], base["out"], rtol=1e-13, atol=1e-14)
+    # a zero projection gives equal probabilities: the mean of the blocks
+    z = oracle.attn_res_forward(stacked, None, w, np.zeros(H), 1e-3, lib=lib)
+    np.testing.assert_allclose(z["out"], stacked.mean(axis=1), rtol=1e-13, atol=1e-15)
+    # identical blocks: out is that block
+    same = np.repeat(prefix[:, None, :], 3, axis=1)
+    np.testing.assert_allclose(oracle.attn_res_forward(same, None, w, p, 1e-3, lib=lib)["out"], prefix,
+                               rtol=1e-14, atol=1e-15)
+    # eps = 0: RMSNorm ignores a block's scale, so scaling block 1 by k keeps
+    # the probabilities and adds P_1 (k - 1) x_1 to the output
+    e0 = oracle.attn_res_forward(stacked, None, w, p, 0.0, lib=lib)
+    sc = stacked.copy()
+    sc[:, 1] *= 7.5
+    e1 = oracle.attn_res_forward(sc, None, w, p, 0.0, lib=lib)
+    np.testing.assert_allclose(e1["probs"], e0["probs"], rtol=1e-13)
+    np.testing.assert_allclose(e1["out"], e0["out"] + e0["probs"][:, 1:2] * 6.5 * stacked[:, 1], rtol=1e-12,
+                               atol=1e-13)
+    # a projection aligned with one block's normalised row and scaled up makes
+    # that block win: out tends to its raw values (not the normalised ones)
+    tgt = stacked[0, 2] / w * 50.0
+    big = oracle.attn_res_forward(stacked[:1], None, w, tgt, 0.0, lib=lib)
+    np.testing.assert_allclose(big["out"][0], stacked[0, 2], rtol=1e-9, atol=1e-9)
+    assert big["probs"][0, 2] > 1 - 1e-12
+    # the magnitudes the tests scale tolerances with
+    np.testing.assert_allclose(base["scale"], np.einsum("tb,tbh->th", base["probs"], np.abs(stacked)),
+                               rtol=1e-13)
+    assert np.all(base["absdot"] >= np.abs(base["logits"]) - 1e-12)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

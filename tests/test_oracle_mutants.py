@@ -1,6 +1,7 @@
 """Planted mistakes in the oracle must be caught by the pins.
 
-Each mutant is a copy of oracle/situ_oracle.c or oracle/mx_oracle.c with one
+Each mutant is a copy of oracle/situ_oracle.c, oracle/mx_oracle.c or
+oracle/attn_res_oracle.c with one
 plausible slip (a dropped term, a wrong sign, a swapped operand or index, the
 wrong rounding, a wrong format constant),
 compiled with gcc into a temporary directory.  The mistakes are planted in the
@@ -17,6 +18,7 @@ from oracle_pins import ALL_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "situ_oracle.c")
 MX_SRC = os.path.join(os.path.dirname(oracle.__file__), "mx_oracle.c")
+ARES_SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_res_oracle.c")
 
 MUTANTS = {
     "sech2_as_one_minus_tanh2": (
@@ -86,10 +88,27 @@ MX_MUTANTS = {
 }
 
 
+ARES_MUTANTS = {
+    "rmsnorm_without_eps": ("sqrt(ss / (double)H + eps)", "sqrt(ss / (double)H)"),
+    "rmsnorm_sum_not_mean": ("sqrt(ss / (double)H + eps)", "sqrt(ss + eps)"),
+    "rmsnorm_not_inverted": ("double r = 1.0 / sqrt(", "double r = sqrt("),
+    "norm_weight_dropped": ("double n = x * r * norm_w[h];", "double n = x * r;"),
+    "logit_from_raw_values": ("dot += n * proj_w[h];", "dot += x * proj_w[h];"),
+    "softmax_not_normalised": ("        P[b] /= den;\n", ""),
+    "softmax_sign_flipped": ("P[b] = exp(l[b] - lmax);", "P[b] = exp(lmax - l[b]);"),
+    "combine_normalised_values": ("o += P[b] * x;", "o += P[b] * x * norm_w[h];"),
+    "prefix_ignored": ("const int64_t nb = m + (has_prefix ? 1 : 0);", "const int64_t nb = m;"),
+    "always_block_zero": ("return blocks[(t * m + b) * H + h];", "return blocks[(t * m) * H + h];"),
+    "prefix_row_index": ("return prefix[t * H + h];", "return prefix[h];"),
+}
+
+
 def _build_mutant(name, tmp):
     mx = name in MX_MUTANTS
-    old, new = (MX_MUTANTS if mx else MUTANTS)[name]
-    with open(MX_SRC if mx else SRC) as f:
+    ares = name in ARES_MUTANTS
+    table = MX_MUTANTS if mx else ARES_MUTANTS if ares else MUTANTS
+    old, new = table[name]
+    with open(MX_SRC if mx else ARES_SRC if ares else SRC) as f:
         text = f.read()
     assert text.count(old) == 1, f"mutation site for {name} not unique/found"
     path = os.path.join(tmp, f"m_{name}.c")
@@ -98,10 +117,12 @@ def _build_mutant(name, tmp):
     out = os.path.join(tmp, f"libm_{name}.so")
     if mx:
         return oracle.build(mx_src=path, out=out)
+    if ares:
+        return oracle.build(ares_src=path, out=out)
     return oracle.build(src=path, out=out)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(MX_MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(MX_MUTANTS) + sorted(ARES_MUTANTS))
 def test_mutant_is_caught(name):
     with tempfile.TemporaryDirectory() as tmp:
         lib = oracle.load(_build_mutant(name, tmp))
