@@ -6,8 +6,9 @@
 One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
 inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
-forward with MXFP8 output instead (forward only).  W untimed steps, then K
-timed steps between two device synchronisations.  Prints ONE JSON line:
+forward with MXFP8 output instead (forward only); attn_res_mix times the
+attention-residual mixing kernel.  W untimed steps, then K timed steps
+between two device synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
                the method must move (every input read once, every output
@@ -39,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "ffn_gated_activation_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_kernels.hip")
 MX_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_mx.hip")
+ARES_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_attn_res.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -96,6 +98,91 @@ def _cpu_baseline(workload: str, sample_rows: int) -> dict:
             "rows_per_s": round(sample_rows / dt, 1)}
 
 
+def _copy_calibration(args, dev):
+    """A plain device copy of known size, for the HBM counter calibration runs."""
+    if not args.copy_calibration_mib:
+        return
+    import torch
+    n = args.copy_calibration_mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def _cpu_baseline_attn_res(name: str) -> dict:
+    import oracle
+    from ffn_gated_activation_amd.workloads import ATTN_RES, attn_res_bytes, make_attn_res_inputs
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    w = ATTN_RES[name]
+    x = make_attn_res_inputs(w.tokens, w.stored, w.hidden, True, dtype=w.dtype, device="cpu", seed=0, eps=w.eps)
+    args = [t.double().numpy() for t in (x["blocks"], x["prefix"], x["norm_weight"], x["proj_weight"])]
+    t0 = time.perf_counter()
+    oracle.attn_res_forward(*args, w.eps, threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(attn_res_bytes(name) / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{name} recipe, all {w.tokens} tokens (seed 0, drawn on the host), fp64, {dt:.2f} s wall",
+            "tokens_per_s": round(w.tokens / dt, 1)}
+
+
+def bench_attn_res(args) -> int:
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_attn_res_fwd
+    from ffn_gated_activation_amd.workloads import ATTN_RES, attn_res_bytes, make_attn_res_inputs
+    w = ATTN_RES[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_attn_res_inputs(w.tokens, w.stored, w.hidden, True, dtype=w.dtype, device=dev, seed=0, eps=w.eps)
+    out = torch.empty(w.tokens, w.hidden, dtype=w.dtype, device=dev)
+
+    def step():
+        situ_glu_attn_res_fwd(x["blocks"], x["prefix"], x["norm_weight"], x["proj_weight"], w.eps, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(args.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    k_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    _copy_calibration(args, dev)
+    nbytes = attn_res_bytes(args.workload)
+    ms = wall / args.steps * 1e3
+    value = nbytes / (ms / 1e3) / 1e9
+    achieved = nbytes / (k_ms / 1e3) / 1e9
+    rec = {
+        "metric": "attention-residual mixing achieved HBM GB/s (% of MI355X peak) and tokens/s, bf16",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "tokens": w.tokens, "blocks": w.stored + 1,
+                   "hidden": w.hidden, "eps": w.eps, "algorithmic_bytes_per_step": nbytes},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
+        "kernels": {"attn_res": {"ms": round(k_ms, 5), "bytes": nbytes, "GB/s": round(achieved, 2)}},
+        "roofline": {"bound": "hbm", "kernel": "situ_glu_attn_res_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(args.workload, "attn_res", ARES_KERNEL_SOURCE)},
+        "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline_attn_res(args.workload),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +204,13 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+
+    from ffn_gated_activation_amd.workloads import ATTN_RES
+    if args.workload in ATTN_RES:
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return bench_attn_res(args)
 
     from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd, situ_glu_fwd_mxfp8
     from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
@@ -179,13 +273,7 @@ def main(argv=None) -> int:
     fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
     bwd_ms = ev[1].elapsed_time(ev[2]) / args.steps if w.backward else 0.0
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+    _copy_calibration(args, dev)
 
     ab = algorithmic_bytes(args.workload)
     ms_per_step = wall / args.steps * 1e3

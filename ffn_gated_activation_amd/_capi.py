@@ -25,12 +25,12 @@ SITU_FP8_E5M2 = 1
 SITU_MX_SCALE_FLOOR = 0
 SITU_MX_SCALE_CEIL = 1
 SITU_MX_BLOCK = 32
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every symbol include/situ_glu.h declares
 EXPORTED = ("situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes",
             "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window",
-            "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize")
+            "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize", "situ_glu_attn_res_fwd")
 
 
 class SituGluError(RuntimeError):
@@ -62,6 +62,8 @@ def _bind(lib):
     lib.situ_glu_fwd_mxfp8.argtypes = [vp, i32, i64, i64, vp, i32, i64, dbl, dblp, i32, i32, vp, vp, vp]
     lib.situ_glu_mx_quantize.restype = i32
     lib.situ_glu_mx_quantize.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
+    lib.situ_glu_attn_res_fwd.restype = i32
+    lib.situ_glu_attn_res_fwd.argtypes = [vp, i64, i64, i64, vp, i32, vp, vp, i32, dbl, vp, i32, vp]
     return lib
 
 

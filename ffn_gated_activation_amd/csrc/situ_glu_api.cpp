@@ -554,4 +554,70 @@ int situ_glu_mx_quantize(const void *x, int io_dtype, int64_t rows, int64_t cols
     return SITU_OK;
 }
 
+int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks, int64_t hidden, const void *prefix,
+                          int io_dtype, const void *norm_weight, const void *proj_weight, int w_dtype, double eps,
+                          void *out, int out_dtype, void *stream)
+{
+    g_last_error.clear();
+    if (!dtype_ok(io_dtype) || !dtype_ok(w_dtype) || !dtype_ok(out_dtype))
+        return fail(SITU_ERR_INVALID_ARG, "dtypes must be SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1) (io %d, w %d, out %d)",
+                    io_dtype, w_dtype, out_dtype);
+    if (!(std::isfinite(eps) && eps >= 0.0))
+        return fail(SITU_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", eps);
+    if (tokens < 0 || nblocks < 0 || hidden < 0)
+        return fail(SITU_ERR_INVALID_ARG, "negative size (tokens=%lld, nblocks=%lld, hidden=%lld)", (long long)tokens,
+                    (long long)nblocks, (long long)hidden);
+    if (hidden > (int64_t)0x3fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "hidden %lld exceeds 2^30 - 1", (long long)hidden);
+    if (tokens > (int64_t)0x7fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "tokens %lld exceeds 2^31 - 1", (long long)tokens);
+    if (tokens == 0 || hidden == 0)
+        return SITU_OK;
+    const int64_t nb = nblocks + (prefix ? 1 : 0);
+    if (nb < 1 || nb > 16)
+        return fail(SITU_ERR_INVALID_ARG, "the values must hold 1 to 16 blocks (got %lld)", (long long)nb);
+    if (nblocks > 0 && !blocks)
+        return fail(SITU_ERR_INVALID_ARG, "blocks is NULL");
+    if (!norm_weight || !proj_weight)
+        return fail(SITU_ERR_INVALID_ARG, "norm_weight or proj_weight is NULL");
+    if (!out)
+        return fail(SITU_ERR_INVALID_ARG, "out is NULL");
+    const int64_t es = dtype_bytes(io_dtype), ws = dtype_bytes(w_dtype), os = dtype_bytes(out_dtype);
+    if ((blocks && !aligned_to(blocks, es)) || (prefix && !aligned_to(prefix, es)))
+        return fail(SITU_ERR_INVALID_ARG, "blocks or prefix is not aligned to its element size");
+    if (!aligned_to(norm_weight, ws) || !aligned_to(proj_weight, ws))
+        return fail(SITU_ERR_INVALID_ARG, "a weight is not aligned to its element size");
+    if (!aligned_to(out, os))
+        return fail(SITU_ERR_INVALID_ARG, "out is not aligned to its element size");
+    const Range o = range("out", out, tokens * hidden * os);
+    const Range ins[] = {range("blocks", blocks, nblocks ? tokens * nblocks * hidden * es : 0),
+                         range("prefix", prefix, prefix ? tokens * hidden * es : 0),
+                         range("norm_weight", norm_weight, hidden * ws), range("proj_weight", proj_weight, hidden * ws)};
+    for (const Range &i : ins)
+        if (overlaps(o, i))
+            return fail(SITU_ERR_INVALID_ARG, "out overlaps input %s", i.name);
+
+    situ::AresLaunch L{};
+    L.blocks = blocks;
+    L.prefix = prefix;
+    L.tokens = tokens;
+    L.m = (int)nblocks;
+    L.nb = (int)nb;
+    L.hidden = (int)hidden;
+    L.norm_w = norm_weight;
+    L.proj_w = proj_weight;
+    L.w_bf16 = w_dtype == SITU_DTYPE_BF16;
+    L.eps = (float)eps;
+    L.out = out;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.out_io = out_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = (!blocks || aligned16(blocks)) && (!prefix || aligned16(prefix)) && aligned16(out) &&
+            aligned16(norm_weight) && aligned16(proj_weight) && (hidden * es) % 16 == 0 &&
+            hidden * 4 < ((int64_t)1 << 31);
+    const int err = situ::launch_attn_res(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "attention-residual launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
 }  // extern "C"

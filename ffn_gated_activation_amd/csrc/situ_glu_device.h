@@ -332,7 +332,7 @@ struct Shape {
     int waves_per_row;
 };
 
-Shape shape(int64_t rows, int inter, int io, int vec, int rows_per_block, int unroll)
+[[maybe_unused]] Shape shape(int64_t rows, int inter, int io, int vec, int rows_per_block, int unroll)
 {
     const int kStrip = 64 * unroll;
     Shape s;

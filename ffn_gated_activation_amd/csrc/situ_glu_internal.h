@@ -109,11 +109,34 @@ struct MxQuantLaunch {
     int rows_per_block;
 };
 
+// Attention-residual mixing: values = blocks [tokens, m, hidden] followed by
+// prefix [tokens, hidden] (when not NULL) along the block axis, nb = m (+1).
+struct AresLaunch {
+    const void *blocks;
+    const void *prefix;
+    int64_t tokens;
+    int m;
+    int nb;
+    int hidden;
+    const void *norm_w;
+    const void *proj_w;
+    int w_bf16;
+    float eps;
+    void *out;
+    int io;               // values' dtype
+    int out_io;           // output dtype
+    int vec;              // 16-byte aligned buffers, rows a whole number of 128-bit vectors
+};
+// Which kernel serves a shape: 0 element path; 1, 3 one 128-bit vector per
+// lane (up to 12 / 16 blocks); 2 two vectors per lane; 4 the streaming kernel.
+int attn_res_path(int io, int hidden, int nb, int vec_ok);
+
 // Enqueue the kernels; return the hipError_t of the launches (0 = success).
 int launch_fwd(const FwdLaunch &L, void *stream);
 int launch_bwd(const BwdLaunch &L, void *stream);
 int launch_fwd_mx(const FwdMxLaunch &L, void *stream);
 int launch_mx_quant(const MxQuantLaunch &L, void *stream);
+int launch_attn_res(const AresLaunch &L, void *stream);
 // Zero `bytes` bytes at device pointer p with a fill kernel.
 int launch_zero(void *p, int64_t bytes, void *stream);
 const char *device_error_string(int err);

@@ -197,6 +197,67 @@ def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: 
     return codes, scales
 
 
+def situ_glu_attn_res_fwd(blocks: torch.Tensor | None, prefix: torch.Tensor | None, norm_weight: torch.Tensor,
+                          proj_weight: torch.Tensor, eps: float, out_dtype: torch.dtype | None = None,
+                          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Attention-residual mixing of the values = blocks [T, m, H] followed by
+    prefix [T, H] (either may be None) along the block axis: RMSNorm (weight
+    norm_weight, epsilon eps), projection to one logit per block
+    (proj_weight), softmax over the blocks, and the weighted sum of the raw
+    values.  Returns [T, H] in out_dtype (default: the values' dtype)."""
+    lib = _capi.load()
+    _check_device(blocks, prefix, norm_weight, proj_weight, out)
+    ref = blocks if blocks is not None else prefix
+    if ref is None:
+        raise ValueError("attention-residual mixing needs blocks or a prefix")
+    io = _io_dtype(ref, "values")
+    if blocks is not None:
+        if blocks.dim() != 3 or not blocks.is_contiguous():
+            raise ValueError(f"blocks must be a contiguous [tokens, blocks, hidden] tensor, got {tuple(blocks.shape)}")
+        tokens, m, hidden = blocks.shape
+    else:
+        m = 0
+    if prefix is not None:
+        if prefix.dtype != ref.dtype or prefix.dim() != 2 or not prefix.is_contiguous():
+            raise ValueError("prefix must be a contiguous [tokens, hidden] tensor of the blocks' dtype")
+        if blocks is not None and tuple(prefix.shape) != (tokens, hidden):
+            raise ValueError(f"prefix must be [{tokens}, {hidden}], got {tuple(prefix.shape)}")
+        tokens, hidden = prefix.shape
+    wd = _io_dtype(norm_weight, "norm_weight")
+    if proj_weight.dtype != norm_weight.dtype:
+        raise TypeError("norm_weight and proj_weight must share a dtype")
+    for w, name in ((norm_weight, "norm_weight"), (proj_weight, "proj_weight")):
+        if w.numel() != hidden or not w.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of {hidden} values")
+    out_dtype = ref.dtype if out_dtype is None else out_dtype
+    od = _io_dtype(torch.empty(0, dtype=out_dtype), "out_dtype")
+    if out is None:
+        out = torch.empty(tokens, hidden, dtype=out_dtype, device=ref.device)
+    elif out.dtype != out_dtype or tuple(out.shape) != (tokens, hidden) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{tokens}, {hidden}] tensor of {out_dtype}")
+    _capi.check(lib.situ_glu_attn_res_fwd(
+        blocks.data_ptr() if blocks is not None else None, tokens, m, hidden,
+        prefix.data_ptr() if prefix is not None else None, io, norm_weight.data_ptr(), proj_weight.data_ptr(), wd,
+        float(eps), out.data_ptr(), od, _stream()), lib)
+    return out
+
+
+def attn_res_core(values: torch.Tensor, norm_weight: torch.Tensor, proj_weight: torch.Tensor,
+                  variance_epsilon: float, out_dtype: torch.dtype) -> torch.Tensor:
+    """The NeMo page's `_attn_res_core(values, norm_weight, proj_weight,
+    variance_epsilon, out_dtype)`: values [T, B+1, H] already stacked."""
+    return situ_glu_attn_res_fwd(values, None, norm_weight, proj_weight, variance_epsilon, out_dtype)
+
+
+def apply_attn_res(prefix_sum: torch.Tensor, block_residual: torch.Tensor, norm_weight: torch.Tensor,
+                   proj_weight: torch.Tensor, eps: float, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """The NeMo page's `_apply_attn_res(prefix_sum, block_residual, ...)`: the
+    stored sums [T, m, H] and the running sum [T, H], mixed without
+    concatenating them first."""
+    return situ_glu_attn_res_fwd(block_residual, prefix_sum.reshape(-1, prefix_sum.shape[-1]), norm_weight,
+                                 proj_weight, eps, out_dtype)
+
+
 def situ_glu_last_error() -> str:
     return _capi.last_error()
 

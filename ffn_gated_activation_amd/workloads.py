@@ -34,6 +34,16 @@ torch's round-to-nearest-even; "N(0, s)" means s * randn):
                 the routed_top8 inputs (same draws), forward only, with the
                 output written as MXFP8 (E4M3 elements, 32-value blocks,
                 floor scale rule) instead of bf16.
+
+Attention-residual mixing (make_attn_res_inputs; draws in the order stored
+sums -> prefix -> norm weight -> projection weight, fp32, then rounded):
+
+  attn_res_mix  8192 tokens, 8 stored block sums + the running prefix sum
+                (9 blocks, the most a Kimi-K3 layer mixes: its 93 layers in
+                blocks of 12), hidden 7168, bf16 values / weights / output;
+                stored sum b ~ N(0, 2^(b/2)) (sums of more layers are larger),
+                prefix ~ N(0, 2); RMSNorm weight 1 + N(0, 0.1); projection
+                weight N(0, 2/sqrt(7168)) (logits of order 2); eps 1e-6.
 """
 from __future__ import annotations
 
@@ -157,3 +167,47 @@ def algorithmic_bytes(name: str, rows: int | None = None) -> dict:
         if w.want_drw:
             bwd += rw_bytes
     return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}
+
+
+@dataclass(frozen=True)
+class AttnResWorkload:
+    name: str
+    tokens: int
+    stored: int          # stored block sums; the prefix sum is one more block
+    hidden: int
+    dtype: torch.dtype
+    eps: float
+    description: str
+
+
+ATTN_RES = {
+    "attn_res_mix": AttnResWorkload("attn_res_mix", 8192, 8, 7168, torch.bfloat16, 1e-6,
+                                    "attention-residual mixing, 8192 tokens x (8 stored sums + prefix) x 7168, "
+                                    "bf16 values/weights/output"),
+}
+
+
+def make_attn_res_inputs(tokens: int, stored: int, hidden: int, prefix: bool = True, dtype=torch.bfloat16,
+                         w_dtype=torch.bfloat16, device="cpu", seed: int = 0, eps: float = 1e-6) -> dict:
+    """Seeded inputs for attention-residual mixing (recipe in the module doc)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32)
+
+    scale = torch.exp2(torch.arange(stored, device=dev, dtype=torch.float32) / 2).reshape(1, stored, 1)
+    blocks = (randn(tokens, stored, hidden) * scale).to(dtype)
+    pre = (2.0 * randn(tokens, hidden)).to(dtype) if prefix else None
+    norm_w = (1.0 + 0.1 * randn(hidden)).to(w_dtype)
+    proj_w = (randn(hidden) * (2.0 / hidden ** 0.5)).to(w_dtype)
+    return {"blocks": blocks, "prefix": pre, "norm_weight": norm_w, "proj_weight": proj_w, "eps": eps}
+
+
+def attn_res_bytes(name: str) -> int:
+    """Bytes the mixing must move: every value read once, both weights once,
+    the output written once."""
+    w = ATTN_RES[name]
+    s = torch.finfo(w.dtype).bits // 8
+    return w.tokens * (w.stored + 1) * w.hidden * s + 2 * w.hidden * s + w.tokens * w.hidden * s

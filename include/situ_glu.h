@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 2
+#define SITU_GLU_ABI_VERSION 3
 
 /* return codes */
 #define SITU_OK 0
@@ -209,6 +209,47 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows,
 int situ_glu_mx_quantize(const void *x, int io_dtype, int64_t rows,
                          int64_t cols, int fp8_format, int scale_mode,
                          void *codes, void *scales, void *stream);
+
+/*
+ * Attention-residual mixing (NeMo AutoModel page
+ * "nemo_automodel.components.models.kimi_k3.situ", `_attn_res_core` and
+ * `_apply_attn_res`; the Kimi-K3 "dense-kda-layers / store" page,
+ * `_forward_attn_residual`, for the call sites).  For every token t the
+ * values are the nblocks stored block sums followed by the current prefix sum
+ * (when prefix is not NULL), NB = nblocks (+ 1) rows of `hidden` values:
+ *     r_b   = 1 / sqrt(mean_h x_bh^2 + eps)                 RMSNorm
+ *     l_b   = sum_h (x_bh r_b norm_weight_h) proj_weight_h   projection
+ *     P     = softmax over b of l                             (over the blocks)
+ *     out_h = sum_b P_b x_bh                                  raw values
+ * computed in fp32 and rounded once to out_dtype.
+ *
+ *   blocks       device pointer, [tokens, nblocks, hidden] of io_dtype (the
+ *                stored sums, or the whole stacked values when prefix is NULL)
+ *   tokens, nblocks, hidden   >= 0; 1 <= NB <= 16 when tokens and hidden are
+ *                not 0; hidden <= 2^30 - 1; tokens <= 2^31 - 1
+ *   prefix       device pointer, [tokens, hidden] of io_dtype (the running
+ *                sum, the last block), or NULL
+ *   io_dtype     SITU_DTYPE_F32 or SITU_DTYPE_BF16 (blocks and prefix)
+ *   norm_weight, proj_weight  device pointers, [hidden] of w_dtype
+ *   w_dtype      SITU_DTYPE_F32 or SITU_DTYPE_BF16
+ *   eps          RMSNorm epsilon, finite and >= 0
+ *   out          device pointer, [tokens, hidden] of out_dtype; must not
+ *                overlap any input
+ *   out_dtype    SITU_DTYPE_F32 or SITU_DTYPE_BF16
+ *   stream       hipStream_t or NULL
+ * 16-byte-aligned buffers with hidden a multiple of 8 (bf16) or 4 (fp32),
+ * hidden * element size < 2^31 and (hidden / values per 16 bytes, NB) within
+ * (1024, 16) or (2048, 8) read every value once; other shapes take a
+ * two-pass element path.  Results are bitwise reproducible and each token's
+ * output depends only on that token's values.  Returns SITU_OK,
+ * SITU_ERR_INVALID_ARG (bad dtype, eps, block count, NULL pointer, negative
+ * size, overlap), SITU_ERR_UNSUPPORTED (too large) or SITU_ERR_DEVICE.
+ */
+int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks,
+                          int64_t hidden, const void *prefix, int io_dtype,
+                          const void *norm_weight, const void *proj_weight,
+                          int w_dtype, double eps, void *out, int out_dtype,
+                          void *stream);
 
 /* Message describing the last error on the calling thread ("" if none). */
 const char *situ_glu_last_error(void);

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 2
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 3
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -152,6 +152,41 @@ def test_mx_quantize_rejects(lib, capi, kw):
     assert capi.last_error(lib) != ""
 
 
+def _ares(lib, **kw):
+    a = dict(blocks=FAKE, tokens=4, m=3, hidden=64, prefix=FAKE + 8192, io=1, w=FAKE + 16384, p=FAKE + 16512,
+             wd=1, eps=1e-6, out=FAKE + 32768, od=1)
+    a.update(kw)
+    return lib.situ_glu_attn_res_fwd(a["blocks"], a["tokens"], a["m"], a["hidden"], a["prefix"], a["io"], a["w"],
+                                     a["p"], a["wd"], a["eps"], a["out"], a["od"], None)
+
+
+# blocks 4 x 3 x 64 x 2 = 1536 bytes at FAKE; prefix 512 bytes at FAKE + 8192;
+# weights 128 bytes each; out 512 bytes at FAKE + 32768
+BAD_ARES = [
+    dict(io=2), dict(wd=-1), dict(od=3), dict(eps=-1e-6), dict(eps=math.nan), dict(eps=math.inf),
+    dict(tokens=-1), dict(m=-1), dict(hidden=-4), dict(m=16), dict(m=0, prefix=None), dict(blocks=None),
+    dict(w=None), dict(p=None), dict(out=None), dict(blocks=FAKE + 1), dict(prefix=FAKE + 8193),
+    dict(w=FAKE + 16385), dict(out=FAKE + 32769, od=0),
+    dict(out=FAKE + 1000),                             # overlaps blocks
+    dict(out=FAKE + 8192 + 256),                       # overlaps prefix
+    dict(out=FAKE + 16384 - 100),                      # overlaps norm_weight
+]
+
+
+@pytest.mark.parametrize("kw", BAD_ARES, ids=[str(k) for k in BAD_ARES])
+def test_attn_res_rejects(lib, capi, kw):
+    assert _ares(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
+    assert capi.last_error(lib) != ""
+
+
+def test_attn_res_empty_and_unsupported(lib, capi):
+    assert _ares(lib, tokens=0, blocks=None, prefix=None, out=None) == capi.SITU_OK
+    assert _ares(lib, hidden=0, blocks=None, prefix=None, out=None) == capi.SITU_OK
+    assert _ares(lib, hidden=1 << 30) == capi.SITU_ERR_UNSUPPORTED
+    assert _ares(lib, tokens=1 << 31) == capi.SITU_ERR_UNSUPPORTED
+    assert _ares(lib, m=15, prefix=None, tokens=0) == capi.SITU_OK
+
+
 def test_mx_empty_and_unsupported(lib, capi):
     # empty calls succeed without touching any pointer
     assert _fwd_mx(lib, rows=0, rw_rows=0, codes=None, scales=None) == capi.SITU_OK
@@ -232,6 +267,14 @@ def test_mx_python_layer_rejects():
         situ_glu_fwd_mxfp8(torch.zeros(2, 64), torch.ones(2, 1))
     with pytest.raises(ValueError):
         situ_glu_mx_quantize(torch.zeros(2, 64))
+
+
+def test_attn_res_python_layer_rejects():
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_attn_res_fwd
+    with pytest.raises(ValueError):
+        situ_glu_attn_res_fwd(torch.zeros(2, 3, 8), torch.zeros(2, 8), torch.ones(8), torch.ones(8), 1e-6)
 
 
 def test_autograd_rejects_cpu_tensors():
