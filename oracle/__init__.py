@@ -6,7 +6,10 @@ arithmetic lives in ``situ_oracle.c`` (the activation and its gradients),
 ``mx_oracle.c`` (MXFP8 block quantisation) and ``attn_res_oracle.c``
 (attention-residual mixing), plain C in double precision with libm, sharing
 nothing with the HIP library.  This module only compiles them
-with gcc, loads them with ctypes and marshals numpy arrays.
+with gcc, loads them with ctypes and marshals numpy arrays; the one
+exception is ``grouped_glu_forward`` (FC1 of routed experts followed by the
+activation), whose projections are a numpy float64 matrix product per expert
+feeding the C activation.
 
 Definitions followed (see the header of ``situ_oracle.c``):
   * Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine", section
@@ -16,6 +19,10 @@ Definitions followed (see the header of ``situ_oracle.c``):
     situ(g)*up(u0)*w), ``_situ_bwd_core`` (analytic dG, dU and the optional
     routing-weight reduction), ``_WeightedSiTUFunction.forward`` (gate first,
     up second in the last axis).
+  * The same Megatron-LM PR, section "Design" (routed experts run FC1 as a
+    grouped GEMM; a SiTU-capable cuDNN frontend fuses that grouped GEMM with
+    the scaled SiTU-GLU): the projections of every expert's rows by that
+    expert's FC1 weight, then the weighted activation of them.
 
 Row blocks can be spread over threads because every row is independent; the
 per-row arithmetic and its order are the C code's, unchanged.
@@ -359,3 +366,49 @@ def attn_res_forward(blocks, prefix, norm_w, proj_w, eps: float, threads: int = 
 
     _run_blocks(run, T, threads)
     return {"out": out, "logits": logits, "probs": probs, "absdot": absdot, "scale": scale}
+
+
+# ----------------------------------------------------------------- grouped FC1 + SiTU-GLU
+
+def grouped_glu_forward(x, w, m_offsets, rw, beta: float = 4.0, linear_beta=25.0, threads: int = 1,
+                        want_terms: bool = True, lib=None) -> dict:
+    """fp64 fused FC1 + weighted SiTU-GLU of routed experts.
+
+    x [M, K] (rows grouped by expert: expert e owns rows m_offsets[e] ..
+    m_offsets[e+1]); w [E, 2I, K] (expert e's FC1 weight, gate rows first);
+    rw [M] (or one weight).  For every expert the projections are
+    gate_up = x_e w_e^T (a float64 matrix product), and the output is the
+    weighted SiTU-GLU of those exact projections (the C oracle's forward).
+
+    Returns out [M, I], gate_up [M, 2I], and (want_terms) the magnitudes a
+    tolerance needs: sG / sU = sum_k |x_k w_k| of every gate / up projection,
+    and the partial derivatives dY/dG, dY/dU of the output."""
+    lib = lib or load()
+    X = _as_f64(x)
+    W = _as_f64(w)
+    E, two_i, K = W.shape
+    inter = two_i // 2
+    M = X.shape[0]
+    off = [int(v) for v in m_offsets]
+    assert len(off) == E + 1 and off[0] == 0 and off[-1] == M
+    gu = np.zeros((M, two_i))
+    s = np.zeros((M, two_i)) if want_terms else None
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        if b > a:
+            gu[a:b] = X[a:b] @ W[e].T
+            if want_terms:
+                s[a:b] = np.abs(X[a:b]) @ np.abs(W[e]).T
+    r = _as_f64(rw).reshape(-1)
+    out = forward(gu, r, beta, linear_beta, threads=threads, lib=lib)
+    res = {"out": out, "gate_up": gu}
+    if want_terms:
+        g, u = gu[:, :inter], gu[:, inter:]
+        rr = np.broadcast_to(r.reshape(-1, 1), (M, 1)) if r.size == M else np.full((M, 1), r[0])
+        vg = np.vectorize(lambda v: gate(v, beta, lib=lib))
+        vgp = np.vectorize(lambda v: gate_grad(v, beta, lib=lib))
+        vu = np.vectorize(lambda v: up(v, linear_beta, lib=lib))
+        vup = np.vectorize(lambda v: up_grad(v, linear_beta, lib=lib))
+        tg, tu = vg(g), vu(u)
+        res.update(sG=s[:, :inter], sU=s[:, inter:], dY_dG=rr * vgp(g) * tu, dY_dU=rr * tg * vup(u))
+    return res

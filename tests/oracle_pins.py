@@ -630,4 +630,39 @@ def pin_ares_invariants(lib):
     assert np.all(base["absdot"] >= np.abs(base["logits"]) - 1e-12)
 
 
+# --------------------------------------------------------------------------
+# grouped FC1 + SiTU-GLU
+# --------------------------------------------------------------------------
+
+def pin_grouped_glu_brute_force(lib):
+    """Tiny problems against triple loops written out: the grouping (rows of
+    expert e use weight e), the gate/up halves of each weight, the routing
+    weight per row, and the derivative terms against finite differences."""
+    rng = np.random.default_rng(47)
+    E, K, I = 3, 5, 2
+    off = [0, 2, 2, 5]                      # expert 1 owns no rows
+    M = off[-1]
+    x = rng.integers(-3, 4, (M, K)).astype(np.float64) / 4
+    w = rng.integers(-3, 4, (E, 2 * I, K)).astype(np.float64) / 4
+    r = rng.uniform(0.1, 1.0, M)
+    res = oracle.grouped_glu_forward(x, w, off, r, 4.0, 25.0, lib=lib)
+    for e in range(E):
+        for m in range(off[e], off[e + 1]):
+            for j in range(I):
+                g = sum(x[m, k] * w[e, j, k] for k in range(K))
+                u = sum(x[m, k] * w[e, I + j, k] for k in range(K))
+                assert abs(res["gate_up"][m, j] - g) < 1e-14 and abs(res["gate_up"][m, I + j] - u) < 1e-14
+                want = r[m] * oracle.gate(g, 4.0, lib=lib) * oracle.up(u, 25.0, lib=lib)
+                _close(res["out"][m, j], want, 1e-14, 1e-15, f"grouped out[{m},{j}]")
+                sg = sum(abs(x[m, k] * w[e, j, k]) for k in range(K))
+                _close(res["sG"][m, j], sg, 1e-14, 1e-15, "sG")
+    # derivative terms: central differences of the output in G and U
+    h = 1e-6
+    for m, j in ((0, 1), (3, 0), (4, 1)):
+        g, u = res["gate_up"][m, j], res["gate_up"][m, I + j]
+        f = lambda gg, uu: r[m] * oracle.gate(gg, 4.0, lib=lib) * oracle.up(uu, 25.0, lib=lib)
+        _close(res["dY_dG"][m, j], (f(g + h, u) - f(g - h, u)) / (2 * h), 1e-6, 1e-9, "dY/dG")
+        _close(res["dY_dU"][m, j], (f(g, u + h) - f(g, u - h)) / (2 * h), 1e-6, 1e-9, "dY/dU")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

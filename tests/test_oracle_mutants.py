@@ -4,7 +4,9 @@ Each mutant is a copy of oracle/situ_oracle.c, oracle/mx_oracle.c or
 oracle/attn_res_oracle.c with one
 plausible slip (a dropped term, a wrong sign, a swapped operand or index, the
 wrong rounding, a wrong format constant),
-compiled with gcc into a temporary directory.  The mistakes are planted in the
+compiled with gcc into a temporary directory, or (the grouped FC1 oracle,
+which is Python) a copy of oracle.grouped_glu_forward with one slip, swapped
+in for the duration of the pins.  The mistakes are planted in the
 CPU oracle only; no GPU code is involved.  A mutant that passes every pin
 would mean the pins cannot see that kind of error.
 """
@@ -101,6 +103,42 @@ ARES_MUTANTS = {
     "always_block_zero": ("return blocks[(t * m + b) * H + h];", "return blocks[(t * m) * H + h];"),
     "prefix_row_index": ("return prefix[t * H + h];", "return prefix[h];"),
 }
+
+
+GROUPED_MUTANTS = {
+    "grouped_always_expert_zero": ("gu[a:b] = X[a:b] @ W[e].T", "gu[a:b] = X[a:b] @ W[0].T"),
+    "grouped_next_expert": ("gu[a:b] = X[a:b] @ W[e].T", "gu[a:b] = X[a:b] @ W[min(e + 1, E - 1)].T"),
+    "grouped_halves_swapped": ("gu[a:b] = X[a:b] @ W[e].T", "gu[a:b] = X[a:b] @ np.roll(W[e], inter, axis=0).T"),
+    "grouped_last_row_dropped": ("a, b = off[e], off[e + 1]", "a, b = off[e], max(off[e + 1] - 1, off[e])"),
+    "grouped_offsets_start_at_one": ("a, b = off[e], off[e + 1]", "a, b = off[e] + (e == 0), off[e + 1]"),
+    "grouped_magnitude_signed_x": ("s[a:b] = np.abs(X[a:b]) @ np.abs(W[e]).T", "s[a:b] = X[a:b] @ np.abs(W[e]).T"),
+    "grouped_dG_without_r": ("dY_dG=rr * vgp(g) * tu", "dY_dG=vgp(g) * tu"),
+    "grouped_dU_uses_gate_grad": ("dY_dU=rr * tg * vup(u)", "dY_dU=rr * vgp(g) * vup(u)"),
+    "grouped_dG_uses_gate": ("dY_dG=rr * vgp(g) * tu", "dY_dG=rr * tg * tu"),
+}
+
+
+def _grouped_mutant(name):
+    import inspect
+    old, new = GROUPED_MUTANTS[name]
+    text = inspect.getsource(oracle.grouped_glu_forward)
+    assert text.count(old) == 1, f"mutation site for {name} not unique/found"
+    ns = dict(vars(oracle))
+    exec(compile(text.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    return ns["grouped_glu_forward"]
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED_MUTANTS))
+def test_grouped_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "grouped_glu_forward", _grouped_mutant(name))
+    lib = oracle.load()
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
 
 
 def _build_mutant(name, tmp):
