@@ -5,7 +5,8 @@
 The host API (csrc/situ_glu_api.cpp, plain C++) is compiled with g++, the
 kernels (csrc/situ_glu_kernels.hip: forward and backward; csrc/situ_glu_mx.hip:
 MXFP8 forward and block quantiser; csrc/situ_glu_attn_res.hip:
-attention-residual mixing) with hipcc for gfx950, in parallel, and all are
+attention-residual mixing; csrc/situ_glu_gemm.hip: fused grouped FC1 GEMM +
+SiTU-GLU on the matrix cores) with hipcc for gfx950, in parallel, and all are
 linked into ffn_gated_activation_amd/libsitu_glu.so.
 """
 from __future__ import annotations
@@ -46,7 +47,7 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-HIP_SOURCES = ("situ_glu_kernels.hip", "situ_glu_mx.hip", "situ_glu_attn_res.hip")
+HIP_SOURCES = ("situ_glu_kernels.hip", "situ_glu_mx.hip", "situ_glu_attn_res.hip", "situ_glu_gemm.hip")
 
 
 def build_library(verbose: bool = False, extra_hipcc: list[str] | None = None, out: str = LIB,

@@ -620,4 +620,70 @@ int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks, i
     return SITU_OK;
 }
 
+int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidden, const void *weight,
+                         int64_t experts, int64_t intermediate, const int32_t *group_offsets,
+                         const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                         const double *linear_beta, void *out, void *gate_up_out, void *stream)
+{
+    g_last_error.clear();
+    if (io_dtype != SITU_DTYPE_BF16)
+        return fail(SITU_ERR_UNSUPPORTED, "the grouped GEMM takes bf16 x and weight only (io_dtype %d)", io_dtype);
+    int rc = check_common(x, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows, beta, linear_beta);
+    if (rc)
+        return rc;
+    if (hidden < 0 || experts < 0)
+        return fail(SITU_ERR_INVALID_ARG, "negative size (hidden=%lld, experts=%lld)", (long long)hidden,
+                    (long long)experts);
+    if (rows == 0 || intermediate == 0)
+        return SITU_OK;
+    if (experts < 1 || experts > SITU_GROUPED_MAX_EXPERTS)
+        return fail(SITU_ERR_INVALID_ARG, "experts must be 1 to %d (got %lld)", SITU_GROUPED_MAX_EXPERTS,
+                    (long long)experts);
+    if (hidden < 64 || hidden % 64 || hidden > SITU_GROUPED_MAX_HIDDEN)
+        return fail(SITU_ERR_UNSUPPORTED, "hidden must be a positive multiple of 64 up to %d (got %lld)",
+                    SITU_GROUPED_MAX_HIDDEN, (long long)hidden);
+    if (intermediate % 128 || intermediate > SITU_GROUPED_MAX_INTERMEDIATE)
+        return fail(SITU_ERR_UNSUPPORTED, "intermediate must be a multiple of 128 up to %d (got %lld)",
+                    SITU_GROUPED_MAX_INTERMEDIATE, (long long)intermediate);
+    if (!weight || !group_offsets || !out)
+        return fail(SITU_ERR_INVALID_ARG, "weight, group_offsets or out is NULL");
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (gate_up_out && !aligned16(gate_up_out)))
+        return fail(SITU_ERR_INVALID_ARG, "x, weight, out and gate_up_out must be 16-byte aligned");
+    if (!aligned_to(group_offsets, 4))
+        return fail(SITU_ERR_INVALID_ARG, "group_offsets is not 4-byte aligned");
+    const Range outs[] = {range("out", out, rows * intermediate * 2),
+                          range("gate_up_out", gate_up_out, gate_up_out ? rows * intermediate * 4 : 0)};
+    const Range ins[] = {range("x", x, rows * hidden * 2), range("weight", weight, experts * 2 * intermediate * hidden * 2),
+                         range("group_offsets", group_offsets, (experts + 1) * 4),
+                         range("routing_weights", routing_weights, rw_rows * dtype_bytes(rw_dtype))};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return fail(SITU_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+    if (overlaps(outs[0], outs[1]))
+        return fail(SITU_ERR_INVALID_ARG, "out overlaps gate_up_out");
+
+    situ::GroupedLaunch L{};
+    L.x = x;
+    L.w = weight;
+    L.offsets = group_offsets;
+    L.rows = rows;
+    L.hidden = (int)hidden;
+    L.experts = (int)experts;
+    L.inter = (int)intermediate;
+    L.rw = routing_weights;
+    L.rw_bf16 = rw_dtype == SITU_DTYPE_BF16;
+    L.rw_stride = rw_rows == rows ? 1 : 0;
+    L.out = out;
+    L.gate_up = gate_up_out;
+    L.lb = linear_beta != nullptr;
+    L.fast = beta == 4.0;
+    L.gk = gate_consts(beta);
+    L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    const int err = situ::launch_grouped_fwd(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "grouped GEMM launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
 }  // extern "C"

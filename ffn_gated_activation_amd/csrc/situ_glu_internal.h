@@ -127,6 +127,30 @@ struct AresLaunch {
     int out_io;           // output dtype
     int vec;              // 16-byte aligned buffers, rows a whole number of 128-bit vectors
 };
+// Fused FC1 grouped GEMM + SiTU-GLU (bf16): x [rows, hidden], w [experts,
+// 2 inter, hidden], offsets [experts + 1] int32 in device memory; hidden a
+// multiple of 64, inter a multiple of 128, all 16-byte aligned.
+struct GroupedLaunch {
+    const void *x;
+    const void *w;
+    const int32_t *offsets;
+    int64_t rows;
+    int hidden;
+    int experts;
+    int inter;
+    const void *rw;
+    int rw_bf16;
+    int64_t rw_stride;
+    void *out;
+    void *gate_up;        // NULL: projections not written
+    int lb;
+    int fast;
+    GateK gk;
+    UpK uk;
+};
+// Row-tile slots of the grouped GEMM grid (floor(rows / 128) + experts).
+int grouped_slots(int64_t rows, int experts);
+
 // Which kernel serves a shape: 0 element path; 1, 3 one 128-bit vector per
 // lane (up to 12 / 16 blocks); 2 two vectors per lane; 4 the streaming kernel.
 int attn_res_path(int io, int hidden, int nb, int vec_ok);
@@ -137,6 +161,7 @@ int launch_bwd(const BwdLaunch &L, void *stream);
 int launch_fwd_mx(const FwdMxLaunch &L, void *stream);
 int launch_mx_quant(const MxQuantLaunch &L, void *stream);
 int launch_attn_res(const AresLaunch &L, void *stream);
+int launch_grouped_fwd(const GroupedLaunch &L, void *stream);
 // Zero `bytes` bytes at device pointer p with a fill kernel.
 int launch_zero(void *p, int64_t bytes, void *stream);
 const char *device_error_string(int err);

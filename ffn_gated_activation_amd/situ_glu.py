@@ -258,6 +258,50 @@ def apply_attn_res(prefix_sum: torch.Tensor, block_residual: torch.Tensor, norm_
                                  proj_weight, eps, out_dtype)
 
 
+def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: torch.Tensor,
+                         routing_weights: torch.Tensor, beta: float = 4.0, linear_beta: float | None = 25.0,
+                         want_gate_up: bool = False, out: torch.Tensor | None = None,
+                         gate_up_out: torch.Tensor | None = None):
+    """Fused FC1 of routed experts + weighted SiTU-GLU.
+
+    x [M, K] bf16 with rows grouped by expert, weight [E, 2I, K] bf16 (each
+    expert's FC1 weight, gate rows first), group_offsets [E + 1] int32 on the
+    device (expert e owns rows group_offsets[e] .. group_offsets[e+1]),
+    routing_weights [M] / [M, 1] or one weight.  Returns out [M, I] bf16, or
+    (out, gate_up [M, 2I] bf16) when want_gate_up."""
+    lib = _capi.load()
+    _check_device(x, weight, group_offsets, routing_weights, out, gate_up_out)
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("the grouped GEMM takes bfloat16 x and weight")
+    if x.dim() != 2 or weight.dim() != 3 or not x.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] and weight a contiguous [E, 2I, K] tensor")
+    rows, hidden = x.shape
+    experts, two_i, k2 = weight.shape
+    if k2 != hidden or two_i % 2:
+        raise ValueError(f"weight must be [E, 2I, {hidden}], got {tuple(weight.shape)}")
+    inter = two_i // 2
+    if group_offsets.dtype != torch.int32 or group_offsets.numel() != experts + 1 or not group_offsets.is_contiguous():
+        raise ValueError(f"group_offsets must be a contiguous int32 tensor of {experts + 1} values")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    rw_rows = routing_weights.numel()
+    if rw_rows not in (rows, 1) or not routing_weights.is_contiguous():
+        raise ValueError(f"routing_weights must hold {rows} row-aligned values or one weight")
+    if out is None:
+        out = torch.empty(rows, inter, dtype=torch.bfloat16, device=x.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, inter) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{rows}, {inter}] bfloat16 tensor")
+    if want_gate_up and gate_up_out is None:
+        gate_up_out = torch.empty(rows, two_i, dtype=torch.bfloat16, device=x.device)
+    if gate_up_out is not None and (gate_up_out.dtype != torch.bfloat16 or tuple(gate_up_out.shape) != (rows, two_i)
+                                    or not gate_up_out.is_contiguous()):
+        raise ValueError(f"gate_up_out must be a contiguous [{rows}, {two_i}] bfloat16 tensor")
+    _capi.check(lib.situ_glu_grouped_fwd(
+        x.data_ptr(), _capi.SITU_DTYPE_BF16, rows, hidden, weight.data_ptr(), experts, inter,
+        group_offsets.data_ptr(), routing_weights.data_ptr(), rwd, rw_rows, float(beta), _capi.lb_ptr(linear_beta),
+        out.data_ptr(), gate_up_out.data_ptr() if gate_up_out is not None else None, _stream()), lib)
+    return (out, gate_up_out) if gate_up_out is not None else out
+
+
 def situ_glu_last_error() -> str:
     return _capi.last_error()
 

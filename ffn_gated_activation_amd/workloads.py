@@ -44,6 +44,19 @@ sums -> prefix -> norm weight -> projection weight, fp32, then rounded):
                 stored sum b ~ N(0, 2^(b/2)) (sums of more layers are larger),
                 prefix ~ N(0, 2); RMSNorm weight 1 + N(0, 0.1); projection
                 weight N(0, 2/sqrt(7168)) (logits of order 2); eps 1e-6.
+
+Fused FC1 grouped GEMM + SiTU-GLU (make_grouped_inputs; draws in the order
+group sizes -> x -> weight -> routing weights):
+
+  grouped_fc1_top8
+                8192 tokens x top-8 = 65536 routed rows over 16 local experts,
+                hidden 7168, expert intermediate 2048 (FC1 weight [16, 4096,
+                7168]); rows per expert = a multinomial draw of 65536 over the
+                probabilities softmax(N(0, 0.5)) of the 16 experts (load
+                imbalance of a real router), rows grouped by expert; x ~ N(0, 1)
+                bf16; weight ~ N(0, 1/sqrt(7168)) bf16 (projections of unit
+                scale); routing weights = softmax over 8 N(0, 1) draws per token
+                (the routed_top8 recipe), fp32; beta 4, linear_beta 25.
 """
 from __future__ import annotations
 
@@ -211,3 +224,64 @@ def attn_res_bytes(name: str) -> int:
     w = ATTN_RES[name]
     s = torch.finfo(w.dtype).bits // 8
     return w.tokens * (w.stored + 1) * w.hidden * s + 2 * w.hidden * s + w.tokens * w.hidden * s
+
+
+@dataclass(frozen=True)
+class GroupedWorkload:
+    name: str
+    rows: int
+    experts: int
+    hidden: int
+    inter: int
+    beta: float
+    linear_beta: float | None
+    description: str
+
+
+GROUPED = {
+    "grouped_fc1_top8": GroupedWorkload("grouped_fc1_top8", 65536, 16, 7168, 2048, 4.0, 25.0,
+                                        "fused FC1 grouped GEMM + SiTU-GLU, 65536 routed rows (8192 tokens x "
+                                        "top-8) over 16 experts, hidden 7168, intermediate 2048, bf16"),
+}
+
+
+def make_grouped_inputs(rows: int, experts: int, hidden: int, inter: int, device="cpu", seed: int = 0,
+                        counts=None, rw_mode: str = "top8") -> dict:
+    """Seeded inputs for the fused grouped GEMM (recipe in the module doc).
+
+    counts: rows per expert (a list summing to rows) instead of the
+    multinomial draw.  rw_mode: "top8" (per-token softmax of 8 draws; rows a
+    multiple of 8), "uniform" (U(0, 1) per row) or "one" (a single weight)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    if counts is None:
+        p = torch.softmax(0.5 * torch.randn(experts, generator=gen, device=dev), 0)
+        idx = torch.multinomial(p, rows, replacement=True, generator=gen) if rows else \
+            torch.zeros(0, dtype=torch.int64, device=dev)
+        counts = torch.bincount(idx, minlength=experts).cpu().tolist()
+    counts = [int(c) for c in counts]
+    if len(counts) != experts or sum(counts) != rows:
+        raise ValueError("counts must hold one count per expert summing to rows")
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+    x = torch.randn(rows, hidden, generator=gen, device=dev).to(torch.bfloat16)
+    w = (torch.randn(experts, 2 * inter, hidden, generator=gen, device=dev) * hidden ** -0.5).to(torch.bfloat16)
+    if rw_mode == "top8":
+        if rows % 8:
+            raise ValueError("top8 routing weights need rows to be a multiple of 8")
+        rw = torch.softmax(torch.randn(rows // 8, 8, generator=gen, device=dev), 1).reshape(rows).contiguous()
+    elif rw_mode == "uniform":
+        rw = torch.rand(rows, generator=gen, device=dev)
+    elif rw_mode == "one":
+        rw = torch.ones(1, device=dev)
+    else:
+        raise ValueError(rw_mode)
+    return {"x": x, "weight": w, "offsets": offsets, "counts": counts, "routing_weights": rw}
+
+
+def grouped_flops(name: str) -> int:
+    """Floating-point operations of the projections: 2 M K (2 I)."""
+    w = GROUPED[name]
+    return 2 * w.rows * w.hidden * 2 * w.inter

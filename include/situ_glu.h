@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 3
+#define SITU_GLU_ABI_VERSION 4
 
 /* return codes */
 #define SITU_OK 0
@@ -250,6 +250,64 @@ int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks,
                           const void *norm_weight, const void *proj_weight,
                           int w_dtype, double eps, void *out, int out_dtype,
                           void *stream);
+
+/* Limits of situ_glu_grouped_fwd. */
+#define SITU_GROUPED_MAX_EXPERTS 4096
+#define SITU_GROUPED_MAX_HIDDEN (1 << 20)
+#define SITU_GROUPED_MAX_INTERMEDIATE (1 << 20)
+
+/*
+ * Fused FC1 of routed experts + weighted SiTU-GLU (Megatron-LM PR "[Dev] Add
+ * SiTU-GLU through Transformer Engine", section "Design": the routed experts'
+ * FC1 is a grouped GEMM, fused with the scaled SiTU-GLU when the backend
+ * supports it; the activation as in section "Activation").  The rows of x
+ * are grouped by expert: expert e owns rows group_offsets[e] ..
+ * group_offsets[e+1] - 1, and for such a row m and j < intermediate
+ *     G = sum_k x[m,k] weight[e,j,k]
+ *     U = sum_k x[m,k] weight[e,intermediate+j,k]
+ *     out[m,j] = r_m * T_g(G) * T_u(U)
+ * with bf16 products summed in fp32 on the matrix cores, the activation
+ * applied to the fp32 sums (they are not rounded to bf16 first), and out
+ * rounded once to bf16.
+ *
+ *   x              device pointer, [rows, hidden] bf16, row major
+ *   io_dtype       SITU_DTYPE_BF16 (the only one supported)
+ *   rows           >= 0, <= 2^31 - 1
+ *   hidden         the contraction length: a multiple of 64, 64 ..
+ *                  SITU_GROUPED_MAX_HIDDEN
+ *   weight         device pointer, [experts, 2*intermediate, hidden] bf16:
+ *                  expert e's FC1 weight, its intermediate gate rows first,
+ *                  then its intermediate up rows (a Linear weight, [out, in])
+ *   experts        1 .. SITU_GROUPED_MAX_EXPERTS
+ *   intermediate   a multiple of 128, <= SITU_GROUPED_MAX_INTERMEDIATE
+ *   group_offsets  device pointer, [experts + 1] int32, non-decreasing from
+ *                  0 to rows.  They are read on the device only (no host
+ *                  synchronisation).  Offsets outside [0, rows] are clamped
+ *                  and a decreasing pair is an empty group: malformed
+ *                  offsets never make the kernel access memory outside the
+ *                  buffers, but rows no group covers are not written and
+ *                  rows that two groups claim get either group's result.
+ *   routing_weights, rw_dtype, rw_rows, beta, linear_beta   as in
+ *                  situ_glu_fwd (rw_rows == rows or 1)
+ *   out            device pointer, [rows, intermediate] bf16
+ *   gate_up_out    device pointer, [rows, 2*intermediate] bf16, or NULL: the
+ *                  projections [G | U] rounded to bf16, the input the
+ *                  backward (situ_glu_bwd) takes
+ *   stream         hipStream_t or NULL
+ * x, weight, out and gate_up_out must be 16-byte aligned; out and gate_up_out
+ * must not overlap each other or any input.  The result of each row depends
+ * only on that row and its expert's weight, and is bitwise reproducible.
+ * Returns SITU_OK, SITU_ERR_INVALID_ARG (bad dtype, beta, count, alignment,
+ * NULL pointer, overlap), SITU_ERR_UNSUPPORTED (a dtype other than bf16, a
+ * shape outside the limits) or SITU_ERR_DEVICE.
+ */
+int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows,
+                         int64_t hidden, const void *weight, int64_t experts,
+                         int64_t intermediate, const int32_t *group_offsets,
+                         const void *routing_weights, int rw_dtype,
+                         int64_t rw_rows, double beta,
+                         const double *linear_beta, void *out,
+                         void *gate_up_out, void *stream);
 
 /* Message describing the last error on the calling thread ("" if none). */
 const char *situ_glu_last_error(void);

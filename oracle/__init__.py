@@ -382,7 +382,8 @@ def grouped_glu_forward(x, w, m_offsets, rw, beta: float = 4.0, linear_beta=25.0
 
     Returns out [M, I], gate_up [M, 2I], and (want_terms) the magnitudes a
     tolerance needs: sG / sU = sum_k |x_k w_k| of every gate / up projection,
-    and the partial derivatives dY/dG, dY/dU of the output."""
+    the partial derivatives dY/dG, dY/dU of the output, and the factors
+    T_g, T_g', T_u, T_u' and r of every output element."""
     lib = lib or load()
     X = _as_f64(x)
     W = _as_f64(w)
@@ -410,5 +411,7 @@ def grouped_glu_forward(x, w, m_offsets, rw, beta: float = 4.0, linear_beta=25.0
         vu = np.vectorize(lambda v: up(v, linear_beta, lib=lib))
         vup = np.vectorize(lambda v: up_grad(v, linear_beta, lib=lib))
         tg, tu = vg(g), vu(u)
-        res.update(sG=s[:, :inter], sU=s[:, inter:], dY_dG=rr * vgp(g) * tu, dY_dU=rr * tg * vup(u))
+        tgp, tup = vgp(g), vup(u)
+        res.update(sG=s[:, :inter], sU=s[:, inter:], dY_dG=rr * vgp(g) * tu, dY_dU=rr * tg * vup(u),
+                   Tg=tg, Tg_prime=tgp, Tu=tu, Tu_prime=tup, r=np.broadcast_to(rr, (M, inter)))
     return res

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 3
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 4
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -177,6 +177,61 @@ BAD_ARES = [
 def test_attn_res_rejects(lib, capi, kw):
     assert _ares(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
     assert capi.last_error(lib) != ""
+
+
+def _grouped(lib, **kw):
+    lb = ctypes.c_double(25.0)
+    a = dict(x=FAKE, io=1, rows=4, hidden=64, w=FAKE + 4096, experts=2, inter=128, off=FAKE + 70000,
+             rw=FAKE + 70016, rwd=0, rw_rows=4, beta=4.0, lb=ctypes.byref(lb), out=FAKE + 73728,
+             gu=FAKE + 81920)
+    a.update(kw)
+    return lib.situ_glu_grouped_fwd(a["x"], a["io"], a["rows"], a["hidden"], a["w"], a["experts"], a["inter"],
+                                    a["off"], a["rw"], a["rwd"], a["rw_rows"], a["beta"], a["lb"], a["out"],
+                                    a["gu"], None)
+
+
+# x 4 x 64 x 2 = 512 bytes at FAKE; weight 2 x 256 x 64 x 2 = 65536 bytes at
+# FAKE + 4096; offsets 12 bytes at FAKE + 70000; routing weights 16 bytes at
+# FAKE + 70016; out 1024 bytes at FAKE + 73728; gate_up 2048 bytes at FAKE + 81920
+BAD_GROUPED = [
+    dict(rwd=3), dict(beta=0.0), dict(beta=math.nan), dict(rows=-1), dict(hidden=-64), dict(experts=-1),
+    dict(experts=0), dict(rw_rows=3), dict(x=None), dict(w=None), dict(off=None), dict(rw=None), dict(out=None),
+    dict(x=FAKE + 8), dict(w=FAKE + 4104), dict(out=FAKE + 73736), dict(gu=FAKE + 81928), dict(off=FAKE + 70002),
+    dict(out=FAKE + 256),                              # overlaps x
+    dict(gu=FAKE + 60000),                             # overlaps the weight
+    dict(out=FAKE + 81920 - 512),                      # overlaps gate_up_out
+    dict(out=FAKE + 70016 - 1008),                     # overlaps the offsets and routing weights
+    dict(experts=4097),
+]
+
+
+@pytest.mark.parametrize("kw", BAD_GROUPED, ids=[str(k) for k in BAD_GROUPED])
+def test_grouped_rejects(lib, capi, kw):
+    assert _grouped(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
+    assert capi.last_error(lib) != ""
+
+
+def test_grouped_empty_and_unsupported(lib, capi):
+    assert _grouped(lib, rows=0, rw_rows=0, x=None, out=None, gu=None) == capi.SITU_OK
+    assert _grouped(lib, inter=0, out=None, gu=None) == capi.SITU_OK
+    assert _grouped(lib, io=0) == capi.SITU_ERR_UNSUPPORTED           # fp32 x
+    assert _grouped(lib, hidden=96) == capi.SITU_ERR_UNSUPPORTED      # not a multiple of 64
+    assert _grouped(lib, hidden=32) == capi.SITU_ERR_UNSUPPORTED
+    assert _grouped(lib, inter=192) == capi.SITU_ERR_UNSUPPORTED      # not a multiple of 128
+    assert _grouped(lib, hidden=capi.SITU_GROUPED_MAX_HIDDEN + 64) == capi.SITU_ERR_UNSUPPORTED
+    assert _grouped(lib, rows=1 << 31, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+
+
+def test_grouped_python_layer_rejects():
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_grouped_fwd
+    with pytest.raises(ValueError):
+        situ_glu_grouped_fwd(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(2, 256, 64, dtype=torch.bfloat16),
+                             torch.zeros(3, dtype=torch.int32), torch.ones(4))
+    with pytest.raises((TypeError, ValueError)):
+        situ_glu_grouped_fwd(torch.zeros(4, 64), torch.zeros(2, 256, 64), torch.zeros(3, dtype=torch.int32),
+                             torch.ones(4))
 
 
 def test_attn_res_empty_and_unsupported(lib, capi):
