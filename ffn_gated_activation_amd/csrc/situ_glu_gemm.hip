@@ -16,18 +16,22 @@
 //   later backward.
 //
 // Tiling (CDNA4, 64-wide wavefronts):
-//   * a workgroup of 256 threads (4 wavefronts) computes a tile of kBM = 128
+//   * a workgroup of 256 threads (4 wavefronts) computes a tile of kBM = 256
 //     rows x kBN = 128 output columns, i.e. 128 gate and the 128 matching up
-//     projection columns.  Wavefront (wm, wn) owns rows wm*64.. and output
-//     columns wn*64..: 2 x 2 blocks of 32 x 32 for G and the same for U, 8
-//     accumulators of v_mfma_f32_32x32x16_bf16.  G and U of one output
-//     element sit in the same lane and register, so the activation is applied
-//     on the accumulators directly.
-//   * the hidden axis is consumed in stages of kBK = 64: x and w tiles are
-//     loaded from global memory into registers one stage ahead and written to
-//     one of two LDS buffers (rows padded to 144 bytes so that the 16-byte
-//     fragment reads of 32 consecutive rows fall in distinct banks); one
-//     barrier per stage.
+//     projection columns.  Wavefront (wm, wn) owns rows wm*128.. and output
+//     columns wn*64..: 4 x 2 blocks of 32 x 32 for G and the same for U, 16
+//     accumulators of v_mfma_f32_32x32x16_bf16 (the whole accumulation
+//     register file).  G and U of one output element sit in the same lane and
+//     register, so the activation is applied on the accumulators directly.
+//     Per 16-wide k step a wavefront reads 8 operand fragments from LDS for
+//     16 matrix instructions.
+//   * the hidden axis is consumed in stages of kBK: the x and w rows of a
+//     stage go from global memory straight into LDS (16-byte buffer loads
+//     that write LDS, no register staging), one stage ahead of the one being
+//     multiplied; one barrier per stage.  Rows are not padded:
+//     chunk c (16 bytes) of row R is stored at chunk c ^ f(R), a swizzle
+//     under which the fragment reads of 16 consecutive rows hit distinct
+//     banks.
 //   * the epilogue stages the bf16 results in LDS and writes whole 16-byte
 //     vectors of each row.
 //
@@ -37,6 +41,8 @@
 // next expert's and need at most floor(M / kBM) + E slots in total; a slot
 // past an expert's rows exits at once.  Each workgroup finds its expert with
 // one parallel comparison over the offsets.
+#include <type_traits>
+
 #include "situ_glu_device.h"
 
 namespace situ {
@@ -45,27 +51,31 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;               // rows of a tile
+constexpr int kBM = 256;               // rows of a tile
 constexpr int kBN = 128;               // output columns of a tile
-constexpr int kBK = 64;                // hidden elements per stage
+constexpr int kBK = 64;                // hidden elements per stage (two stage buffers)
 constexpr int kThreads = 256;
-constexpr int kRowBytes = kBK * 2 + 16;             // padded LDS row: 144 bytes
+constexpr int kCh = kBK / 8;                        // 16-byte chunks of a row in one stage
+constexpr int kRowB = kBK * 2;                      // bytes of a row in one stage
+constexpr int kRowsPerBank = 256 / kRowB;           // rows per 256 bytes (the bank period)
 constexpr int kARows = kBM, kBRows = 2 * kBN;       // x rows, then gate rows and up rows
-constexpr int kStageBytes = (kARows + kBRows) * kRowBytes;  // 55296
-constexpr int kYRowBytes = kBN * 2 + 16;            // epilogue staging row of Y (272 bytes)
-constexpr int kGuRowBytes = 2 * kBN * 2 + 16;       // epilogue staging row of G|U (528 bytes)
-static_assert(kBM * (kYRowBytes + kGuRowBytes) <= 2 * kStageBytes, "epilogue staging must fit");
+constexpr int kStageBytes = (kARows + kBRows) * kRowB;
+constexpr int kRowsPerLoad = 64 / kCh;              // rows one wavefront-wide load fills
+constexpr int kLoads = (kARows + kBRows) / kRowsPerLoad / 4;  // loads per thread and stage
+constexpr int kYRowBytes = kBN * 2 + 16;            // epilogue staging row (272 bytes)
+constexpr int kEpiBytes = kBM * kYRowBytes;         // one staged [kBM, kBN] bf16 block
+static_assert(kBK % 16 == 0 && kCh * kRowsPerBank == 16, "the swizzle assumes 16 rows per bank cycle");
+static_assert(kLoads == 2 * kCh, "x and w rows split evenly over the loads");
+constexpr int kBufBytes = kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes;
 #ifndef SITU_GEMM_GROUP_M
 #define SITU_GEMM_GROUP_M 16
 #endif
 constexpr int kGroupM = SITU_GEMM_GROUP_M;          // row tiles of a super tile
 
-__device__ __forceinline__ uint4 gload(rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    // x and w are re-read by other workgroups: default cache policy
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
+using lds_ptr_t = __attribute__((address_space(3))) void *;
+
+// chunk slot of logical chunk c in row r
+__device__ __forceinline__ int swz(int r) { return (r / kRowsPerBank) % kCh; }
 
 // Tile (slot, column tile) of a linear workgroup index: super tiles of
 // kGroupM row slots x all column tiles, row slots fastest inside, so that the
@@ -84,6 +94,15 @@ __device__ __forceinline__ void st_bf16(char *p, float v)
     *reinterpret_cast<uint16_t *>(p) = f32_to_bf16(v);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool LB, bool FAST, bool GU>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__ w,
@@ -91,7 +110,11 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
                             int inter, int slots, const void *__restrict__ rw, int rw_bf16, int64_t rw_stride,
                             void *__restrict__ out, void *__restrict__ gate_up, GateK gk, UpK uk)
 {
-    __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+    // Two stage buffers as two objects: the compiler then knows that loads
+    // landing in one do not alias the fragment reads of the other, and does
+    // not make those reads wait for the loads in flight.
+    __shared__ __attribute__((aligned(1024))) char smem0[kBufBytes];
+    __shared__ __attribute__((aligned(1024))) char smem1[kBufBytes];
     __shared__ float s_rs[kBM];
     __shared__ int s_expert;
 
@@ -123,79 +146,81 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     const int n0 = ct * kBN;
 
     // ---- per-row scale r * b1 (* b2), zero past the tile's rows
-    if (t < kBM) {
+    {
         float r = 0.0f;
         if (t < nrows)
             r = load_rw(rw, rw_bf16, (int64_t)(row0 + t) * rw_stride);
         s_rs[t] = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
     }
 
-    // ---- operand descriptors: the tile's x rows, its gate rows and its up rows
+    // ---- operand descriptors.  Loads of rows 0..kBM-1 of one region: x rows
+    // of the tile (past nrows they read as zero), gate rows 0..kBN-1 and, via
+    // a base kBN rows early, up rows kBN..2kBN-1 of the same offsets.
     const uint32_t kbytes = (uint32_t)hidden * 2u;
     const char *xb = static_cast<const char *>(x) + (int64_t)row0 * kbytes;
     const char *wb = static_cast<const char *>(w) + ((int64_t)e * 2 * inter + n0) * kbytes;
-    const rsrc_t ra = make_rsrc(xb, (uint32_t)nrows * kbytes);  // rows past the tile read as zero
+    const rsrc_t ra = make_rsrc(xb, (uint32_t)nrows * kbytes);
     const rsrc_t rg = make_rsrc(wb, (uint32_t)kBN * kbytes);
-    const rsrc_t ru = make_rsrc(wb + (int64_t)inter * kbytes, (uint32_t)kBN * kbytes);
+    const rsrc_t ru = make_rsrc(wb + ((int64_t)inter - kBN) * kbytes, (uint32_t)(2 * kBN) * kbytes);
 
-    // loader role: 8 threads per 128-byte row segment, 32 rows per pass
-    const int lrow = t >> 3, lch = t & 7;
-    uint32_t voff[4];
+    // loader role: load j of wavefront wv fills rows (4 j + wv) * kRowsPerLoad..
+    // of the 512-row stage (x rows first); lane l takes row + l / kCh and the
+    // logical chunk whose slot is l % kCh.
+    const int lane = t & 63, wv = t >> 6;
+    uint32_t voff[kCh];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        voff[i] = (uint32_t)(lrow + 32 * i) * kbytes + (uint32_t)lch * 16u;
-    const uint32_t lds_w = (uint32_t)lrow * kRowBytes + (uint32_t)lch * 16u;
+    for (int j = 0; j < kCh; ++j) {
+        const int r = (4 * j + wv) * kRowsPerLoad + lane / kCh;
+        voff[j] = (uint32_t)r * kbytes + (uint32_t)(((lane % kCh) ^ swz(r)) * 16);
+    }
+    auto issue = [&](int kt, auto buf) {
+        const uint32_t so = (uint32_t)kt * kRowB;
+        char *base = decltype(buf)::value ? smem1 : smem0;
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) {
+            const int blk = 4 * j + wv;
+            const rsrc_t r = j < kCh ? ra : (j - kCh < kCh / 2 ? rg : ru);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + blk * 1024), 16, (int)voff[j % kCh],
+                                                     (int)so, 0, 0);
+        }
+    };
 
     // compute role
-    const int lane = t & 63, wv = t >> 6;
     const int wm = wv >> 1, wn = wv & 1;
     const int l32 = lane & 31, lh = lane >> 5;
-    const uint32_t a_rd = (uint32_t)(wm * 64 + l32) * kRowBytes + (uint32_t)lh * 16u;
-    const uint32_t g_rd = (uint32_t)(kARows + wn * 64 + l32) * kRowBytes + (uint32_t)lh * 16u;
-    const uint32_t u_rd = g_rd + (uint32_t)kBN * kRowBytes;
+    const int f = swz(l32);  // the swizzle of every row this lane reads (row bases are multiples of 32)
+    uint32_t rda[kBK / 16], rdb[kBK / 16];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const uint32_t c = (uint32_t)(((2 * kk + lh) ^ f) * 16);
+        rda[kk] = (uint32_t)(wm * 128 + l32) * kRowB + c;
+        rdb[kk] = (uint32_t)(kARows + wn * 64 + l32) * kRowB + c;
+    }
 
-    uint4 rx[4], rgw[4], ruw[4];
-    auto fetch = [&](int kt) {
-        const uint32_t so = (uint32_t)kt * (kBK * 2);
+    f32x16 accg[4][2], accu[4][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rx[i] = gload(ra, voff[i], so);
-            rgw[i] = gload(rg, voff[i], so);
-            ruw[i] = gload(ru, voff[i], so);
-        }
-    };
-    auto stash = [&](int buf) {
-        char *s = smem + buf * kStageBytes + lds_w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<uint4 *>(s + (32 * i) * kRowBytes) = rx[i];
-            *reinterpret_cast<uint4 *>(s + (kARows + 32 * i) * kRowBytes) = rgw[i];
-            *reinterpret_cast<uint4 *>(s + (kARows + kBN + 32 * i) * kRowBytes) = ruw[i];
-        }
-    };
-
-    f32x16 accg[2][2], accu[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             accg[i][j] = f32x16{};
             accu[i][j] = f32x16{};
         }
 
-    auto compute = [&](int buf) {
-        const char *s = smem + buf * kStageBytes;
+    auto compute = [&](auto buf) {
+        const char *s = decltype(buf)::value ? smem1 : smem0;
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8 a[2], bg[2], bu[2];
+            bf16x8 a[4], bg[2], bu[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                a[i] = *reinterpret_cast<const bf16x8 *>(s + a_rd + i * 32 * kRowBytes + kk * 32);
-                bg[i] = *reinterpret_cast<const bf16x8 *>(s + g_rd + i * 32 * kRowBytes + kk * 32);
-                bu[i] = *reinterpret_cast<const bf16x8 *>(s + u_rd + i * 32 * kRowBytes + kk * 32);
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8 *>(s + rda[kk] + i * 32 * kRowB);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bg[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + j * 32 * kRowB);
+                bu[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + (kBN + j * 32) * kRowB);
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bg[j], accg[i][j], 0, 0, 0);
@@ -204,67 +229,99 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
         }
     };
 
+    // ---- main loop: stage kt + 1 is in flight while stage kt is multiplied.
+    // Each stage starts with this thread's loads of it complete and a barrier
+    // (everyone's loads landed, the other buffer fully consumed); the next
+    // stage's loads are issued before the multiplications and kept there.
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
     const int nk = hidden / kBK;
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        fetch(kt + 1);
-        // keep the next stage's loads in flight across the whole compute phase
-        __builtin_amdgcn_sched_barrier(0);
-        compute(kt & 1);
-        stash((kt + 1) & 1);
+    issue(0, Buf0{});
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+        wait_vmcnt<0>();
         __syncthreads();
+        issue(kt + 1, Buf1{});
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Buf0{});
+        wait_vmcnt<0>();
+        __syncthreads();
+        issue(kt + 2, Buf0{});
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Buf1{});
     }
-    compute((nk - 1) & 1);
+    // stage kt (buffer 0) is in flight; kt + 1 is the last one, if any
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + 1 < nk)
+        issue(kt + 1, Buf1{});
+    __builtin_amdgcn_sched_barrier(0);
+    compute(Buf0{});
+    if (kt + 1 < nk) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        compute(Buf1{});
+    }
     __syncthreads();  // every wavefront is done with the stage buffers
 
     // ---- epilogue: activation on the accumulators, staged through LDS as bf16
-    char *sy = smem;                            // [kBM][kYRowBytes]
-    char *sgu = smem + kBM * kYRowBytes;        // [kBM][kGuRowBytes]
+    char *sy = smem0;
+    char *sg = smem1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 // MFMA 32x32 result layout: register r of lane l holds row
                 // (r/4)*8 + (l/32)*4 + r%4, column l%32 of the block
-                const int row = wm * 64 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                const int row = wm * 128 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
                 const int col = wn * 64 + j * 32 + l32;
                 const float g = accg[i][j][r], u = accu[i][j][r];
                 st_bf16(sy + row * kYRowBytes + col * 2, fwd_elem<LB, FAST, false>(g, u, s_rs[row], gk, uk));
-                if (GU) {
-                    st_bf16(sgu + row * kGuRowBytes + col * 2, g);
-                    st_bf16(sgu + row * kGuRowBytes + (kBN + col) * 2, u);
-                }
+                if (GU)
+                    st_bf16(sg + row * kYRowBytes + col * 2, g);
             }
     __syncthreads();
 
-    // Y: 16 vectors of 16 bytes per row, 16 rows per pass
+    // whole rows of 16 vectors of 16 bytes, 16 rows per pass; rows past the
+    // tile fall outside the descriptors and their stores are dropped
+    const int c16 = t & 15, r16 = t >> 4;
     const uint32_t ybytes = (uint32_t)inter * 2u;
     const rsrc_t ro = make_rsrc(static_cast<char *>(out) + (int64_t)row0 * ybytes, (uint32_t)nrows * ybytes);
-    {
-        const int c = t & 15, r0 = t >> 4;
-#pragma unroll
-        for (int p = 0; p < kBM / 16; ++p) {
-            const int row = r0 + 16 * p;
-            const uint4 v = *reinterpret_cast<const uint4 *>(sy + row * kYRowBytes + c * 16);
-            // rows past the tile fall outside the descriptor: the store is dropped
-            bstore(ro, (uint32_t)row * ybytes + (uint32_t)(n0 * 2 + c * 16), v);
-        }
+#pragma unroll 4
+    for (int p = 0; p < kBM / 16; ++p) {
+        const int row = r16 + 16 * p;
+        const uint4 v = *reinterpret_cast<const uint4 *>(sy + row * kYRowBytes + c16 * 16);
+        bstore(ro, (uint32_t)row * ybytes + (uint32_t)(n0 * 2 + c16 * 16), v);
     }
     if (GU) {
         const uint32_t gbytes = 2u * ybytes;
         const rsrc_t rq =
             make_rsrc(static_cast<char *>(gate_up) + (int64_t)row0 * gbytes, (uint32_t)nrows * gbytes);
-        const int c = t & 31, r0 = t >> 5;   // 16 gate vectors then 16 up vectors per row
-        const uint32_t colb = c < 16 ? (uint32_t)(n0 * 2 + c * 16) : (uint32_t)((inter + n0) * 2 + (c - 16) * 16);
+#pragma unroll 4
+        for (int p = 0; p < kBM / 16; ++p) {
+            const int row = r16 + 16 * p;
+            const uint4 v = *reinterpret_cast<const uint4 *>(sg + row * kYRowBytes + c16 * 16);
+            bstore(rq, (uint32_t)row * gbytes + (uint32_t)(n0 * 2 + c16 * 16), v);
+        }
+        __syncthreads();
 #pragma unroll
-        for (int p = 0; p < kBM / 8; ++p) {
-            const int row = r0 + 8 * p;
-            const uint4 v = *reinterpret_cast<const uint4 *>(sgu + row * kGuRowBytes + c * 16);
-            bstore(rq, (uint32_t)row * gbytes + colb, v);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * 128 + i * 32 + (r >> 2) * 8 + lh * 4 + (r & 3);
+                    const int col = wn * 64 + j * 32 + l32;
+                    st_bf16(sy + row * kYRowBytes + col * 2, accu[i][j][r]);
+                }
+        __syncthreads();
+#pragma unroll 4
+        for (int p = 0; p < kBM / 16; ++p) {
+            const int row = r16 + 16 * p;
+            const uint4 v = *reinterpret_cast<const uint4 *>(sy + row * kYRowBytes + c16 * 16);
+            bstore(rq, (uint32_t)row * gbytes + (uint32_t)((inter + n0) * 2 + c16 * 16), v);
         }
     }
 }

@@ -148,7 +148,7 @@ struct GroupedLaunch {
     GateK gk;
     UpK uk;
 };
-// Row-tile slots of the grouped GEMM grid (floor(rows / 128) + experts).
+// Row-tile slots of the grouped GEMM grid (floor(rows / 256) + experts).
 int grouped_slots(int64_t rows, int experts);
 
 // Which kernel serves a shape: 0 element path; 1, 3 one 128-bit vector per
