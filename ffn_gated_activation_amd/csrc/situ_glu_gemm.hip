@@ -77,16 +77,47 @@ using lds_ptr_t = __attribute__((address_space(3))) void *;
 // chunk slot of logical chunk c in row r
 __device__ __forceinline__ int swz(int r) { return (r / kRowsPerBank) % kCh; }
 
-// Tile (slot, column tile) of a linear workgroup index: super tiles of
-// kGroupM row slots x all column tiles, row slots fastest inside, so that the
-// workgroups in flight share x rows and one expert's weight.
-__device__ __forceinline__ void tile_of(int L, int slots, int ntn, int &rt, int &ct)
+#ifndef SITU_GEMM_XCD
+#define SITU_GEMM_XCD 1
+#endif
+#ifndef SITU_GEMM_XCD_ROWS
+#define SITU_GEMM_XCD_ROWS 8
+#endif
+// Tile (slot, column tile) of workgroup b.  Workgroups are dealt to the 8
+// XCDs round robin (b % 8), each XCD with its own L2, and 256 (one per CU)
+// run at a time.  With the column tiles a multiple of 16, one such wave of
+// 256 covers a super tile of 16 row slots x 16 column tiles, and inside it
+// XCD x takes the 8 x 4 block of rows (x % 2) * 8.. and columns (x / 2) * 4..:
+// its 32 workgroups then share 8 x tiles and 4 weight tiles in its L2 (every
+// stage needs 12 distinct tiles, not 32 x 2).  Otherwise super tiles of
+// kGroupM row slots x all column tiles, row slots fastest.  Returns false
+// for a workgroup past the grid's real tiles.
+__device__ __forceinline__ bool tile_of(int b, int slots, int ntn, int &rt, int &ct)
 {
+    if (SITU_GEMM_XCD && ntn % 16 == 0) {
+        const int x = b & 7, k = b >> 3;
+        const int round = k >> 5, q = k & 31;
+        const int scols = ntn >> 4;
+        const int sr = round / scols, sc = round - sr * scols;
+        constexpr int XR = SITU_GEMM_XCD_ROWS, XC = 32 / XR, NR = 16 / XR;
+        rt = sr * 16 + (x % NR) * XR + q % XR;
+        ct = sc * 16 + (x / NR) * XC + q / XR;
+        return rt < slots;
+    }
     const int per = kGroupM * ntn;
-    const int s = L / per, p = L - s * per;
+    const int s = b / per, p = b - s * per;
     const int gm = min(kGroupM, slots - s * kGroupM);
     rt = s * kGroupM + p % gm;
     ct = p / gm;
+    return true;
+}
+
+// Workgroups in the grid: whole super tiles in the XCD mapping.
+__host__ __device__ inline int64_t grid_blocks(int slots, int ntn)
+{
+    if (SITU_GEMM_XCD && ntn % 16 == 0)
+        return (int64_t)((slots + 15) / 16) * 16 * ntn;
+    return (int64_t)slots * ntn;
 }
 
 __device__ __forceinline__ void st_bf16(char *p, float v)
@@ -121,7 +152,8 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     const int t = threadIdx.x;
     const int ntn = inter / kBN;
     int rt, ct;
-    tile_of(blockIdx.x, slots, ntn, rt, ct);
+    if (!tile_of(blockIdx.x, slots, ntn, rt, ct))
+        return;  // past the last row slot (padding of the last super tile)
 
     // ---- which expert owns row slot rt (the largest match wins on malformed offsets)
     if (t == 0)
@@ -166,20 +198,25 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     // loader role: load j of wavefront wv fills rows (4 j + wv) * kRowsPerLoad..
     // of the 512-row stage (x rows first); lane l takes row + l / kCh and the
     // logical chunk whose slot is l % kCh.
-    const int lane = t & 63, wv = t >> 6;
+    // the wavefront index is uniform: keep it scalar so that the LDS
+    // addresses of the loads (the M0 operand) are scalar arithmetic
+    const int lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
     uint32_t voff[kCh];
 #pragma unroll
     for (int j = 0; j < kCh; ++j) {
         const int r = (4 * j + wv) * kRowsPerLoad + lane / kCh;
         voff[j] = (uint32_t)r * kbytes + (uint32_t)(((lane % kCh) ^ swz(r)) * 16);
     }
-    auto issue = [&](int kt, auto buf) {
+    const int nk = hidden / kBK;
+    const rsrc_t rz = make_rsrc(xb, 0u);  // reads as zero: the padding stage of an odd count
+    auto issue = [&](int kt, auto buf, int j0 = 0, int j1 = kLoads) {
         const uint32_t so = (uint32_t)kt * kRowB;
         char *base = decltype(buf)::value ? smem1 : smem0;
+        const bool live = kt < nk;
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
+        for (int j = j0; j < j1; ++j) {
             const int blk = 4 * j + wv;
-            const rsrc_t r = j < kCh ? ra : (j - kCh < kCh / 2 ? rg : ru);
+            const rsrc_t r = !live ? rz : j < kCh ? ra : (j - kCh < kCh / 2 ? rg : ru);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(base + blk * 1024), 16, (int)voff[j % kCh],
                                                      (int)so, 0, 0);
         }
@@ -206,62 +243,115 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
             accu[i][j] = f32x16{};
         }
 
-    auto compute = [&](auto buf) {
-        const char *s = decltype(buf)::value ? smem1 : smem0;
+    struct Frags {
+        bf16x8 a[4], g[2], u[2];
+    };
+    auto read_frags = [&](const char *s, int kk, Frags &f) {
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8 a[4], bg[2], bu[2];
+        for (int i = 0; i < 4; ++i)
+            f.a[i] = *reinterpret_cast<const bf16x8 *>(s + rda[kk] + i * 32 * kRowB);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(s + rda[kk] + i * 32 * kRowB);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                bg[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + j * 32 * kRowB);
-                bu[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + (kBN + j * 32) * kRowB);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bg[j], accg[i][j], 0, 0, 0);
-                    accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bu[j], accu[i][j], 0, 0, 0);
-                }
+        for (int j = 0; j < 2; ++j) {
+            f.g[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + j * 32 * kRowB);
+            f.u[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + (kBN + j * 32) * kRowB);
         }
     };
-
-    // ---- main loop: stage kt + 1 is in flight while stage kt is multiplied.
-    // Each stage starts with this thread's loads of it complete and a barrier
-    // (everyone's loads landed, the other buffer fully consumed); the next
-    // stage's loads are issued before the multiplications and kept there.
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.g[j], accg[i][j], 0, 0, 0);
+                accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.u[j], accu[i][j], 0, 0, 0);
+            }
+    };
+    // Interleave one k step's 16 products with the 8 fragment reads of the
+    // next step (and, optionally, 16 global loads): a read or a pair of loads
+    // between consecutive products keeps LDS and memory requests flowing
+    // while the matrix core works.
+    auto pattern = [](bool reads, bool loads) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // a product
+            if (loads)
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two global loads
+            if (reads)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    };
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
-    const int nk = hidden / kBK;
+    Frags f0, f1;
+#ifndef SITU_GEMM_SPLIT
+#define SITU_GEMM_SPLIT 8
+#endif
+    constexpr int kFirst = SITU_GEMM_SPLIT;  // loads issued at the boundary, the rest in the next step
+    // k steps 0..2 of a stage: products of step kk, fragments of step kk + 1
+    // (and the remaining loads of stage kt_next into the other buffer)
+    auto first_steps = [&](auto buf, int kt_next) {
+        const char *s = decltype(buf)::value ? smem1 : smem0;
+        read_frags(s, 1, f1);
+        if (kFirst < kLoads)
+            issue(kt_next, std::integral_constant<int, 1 - decltype(buf)::value>{}, kFirst, kLoads);
+        mfmas(f0);
+        if (kFirst < kLoads) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        } else {
+            pattern(true, false);
+        }
+        read_frags(s, 2, f0);
+        mfmas(f1);
+        pattern(true, false);
+        read_frags(s, 3, f1);
+        mfmas(f0);
+        pattern(true, false);
+    };
+    // the stage boundary: once every wavefront has read its last fragments of
+    // the stage in `buf` and its loads of the next stage (other buffer) have
+    // landed, one barrier; then the next stage's first fragments and the
+    // loads of stage kt_next (into `buf`) go out while the last 16 products
+    // of the stage run
+    auto boundary = [&](auto buf, int kt_next) {
+        constexpr int nb = 1 - decltype(buf)::value;
+        wait_vmcnt<0>();
+        __syncthreads();
+        read_frags(nb ? smem1 : smem0, 0, f0);
+        issue(kt_next, buf, 0, kFirst);
+        mfmas(f1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < kFirst)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- main loop.  Stage kt lives in buffer kt % 2; the loads of stage
+    // kt + 1 are in flight while stage kt is multiplied.  The body is two
+    // stages (one per buffer) with no tail: an odd stage count gets one more
+    // stage of zeros (an empty descriptor), which adds nothing.
     issue(0, Buf0{});
-    int kt = 0;
-    for (; kt + 2 < nk; kt += 2) {
-        wait_vmcnt<0>();
-        __syncthreads();
-        issue(kt + 1, Buf1{});
-        __builtin_amdgcn_sched_barrier(0);
-        compute(Buf0{});
-        wait_vmcnt<0>();
-        __syncthreads();
-        issue(kt + 2, Buf0{});
-        __builtin_amdgcn_sched_barrier(0);
-        compute(Buf1{});
-    }
-    // stage kt (buffer 0) is in flight; kt + 1 is the last one, if any
     wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < nk)
-        issue(kt + 1, Buf1{});
-    __builtin_amdgcn_sched_barrier(0);
-    compute(Buf0{});
-    if (kt + 1 < nk) {
-        wait_vmcnt<0>();
-        __syncthreads();
-        compute(Buf1{});
+    read_frags(smem0, 0, f0);
+    issue(1, Buf1{}, 0, kFirst);
+    // (the second half of stage 1's loads: issued with stage 0's first step)
+    for (int kt = 0; kt < nk; kt += 2) {
+        first_steps(Buf0{}, kt + 1);
+        boundary(Buf0{}, kt + 2);
+        first_steps(Buf1{}, kt + 2);
+        boundary(Buf1{}, kt + 3);
     }
+    wait_vmcnt<0>();  // loads past the last stage (zeros) have landed
     __syncthreads();  // every wavefront is done with the stage buffers
 
     // ---- epilogue: activation on the accumulators, staged through LDS as bf16
@@ -281,6 +371,10 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
                 st_bf16(sy + row * kYRowBytes + col * 2, fwd_elem<LB, FAST, false>(g, u, s_rs[row], gk, uk));
                 if (GU)
                     st_bf16(sg + row * kYRowBytes + col * 2, g);
+                // one 32 x 32 block at a time: bounds the registers the
+                // activation takes while all accumulators are still live
+                if (r == 15)
+                    __builtin_amdgcn_sched_barrier(0);
             }
     __syncthreads();
 
@@ -342,7 +436,7 @@ int grouped_slots(int64_t rows, int experts) { return (int)(rows / kBM) + expert
 int launch_grouped_fwd(const GroupedLaunch &L, void *stream)
 {
     const int slots = grouped_slots(L.rows, L.experts);
-    const int64_t blocks = (int64_t)slots * (L.inter / kBN);
+    const int64_t blocks = grid_blocks(slots, L.inter / kBN);
     if (blocks <= 0)
         return 0;
     GemmFn fn = L.lb ? (L.fast ? pick_gu<true, true>(L.gate_up) : pick_gu<true, false>(L.gate_up))
