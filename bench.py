@@ -7,8 +7,10 @@ One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
 inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
 forward with MXFP8 output instead (forward only); attn_res_mix times the
-attention-residual mixing kernel.  W untimed steps, then K timed steps
-between two device synchronisations.  Prints ONE JSON line:
+attention-residual mixing kernel; grouped_fc1_top8 times the fused FC1
+grouped GEMM + SiTU-GLU (value and roofline in TFLOP/s against the bf16
+matrix-core peak).  W untimed steps, then K timed steps between two device
+synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
                the method must move (every input read once, every output
@@ -41,6 +43,8 @@ CSRC = os.path.join(ROOT, "ffn_gated_activation_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_kernels.hip")
 MX_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_mx.hip")
 ARES_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_attn_res.hip")
+GEMM_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_gemm.hip")
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -183,6 +187,117 @@ def bench_attn_res(args) -> int:
     return 0
 
 
+def _cpu_baseline_grouped(name: str, sample_rows: int) -> dict:
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    from ffn_gated_activation_amd.workloads import GROUPED, make_grouped_inputs
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    w = GROUPED[name]
+    x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device="cpu", seed=0)
+    # the first sample_rows rows with their experts' weights (rows are grouped by expert)
+    off = x["offsets"]
+    n = min(sample_rows, w.rows)
+    last = max(e for e in range(w.experts) if off[e] < n)
+    sub_off = [min(o, n) for o in off[:last + 2]]
+    xs = x["x"][:n].double().numpy()
+    ws = x["weight"][:last + 1].double().numpy()
+    rs = x["routing_weights"][:n].double().numpy()
+    del x
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        oracle.grouped_glu_forward(xs, ws, sub_off, rs, w.beta, w.linear_beta, threads=cores, want_terms=False)
+        dt = time.perf_counter() - t0
+    flops = 2 * n * w.hidden * 2 * w.inter
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{name} recipe, first {n} rows ({last + 1} expert(s); seed 0, drawn on the host), fp64 "
+                      f"matrix products per expert + fp64 activation, {dt:.2f} s wall",
+            "rows_per_s": round(n / dt, 1)}
+
+
+def bench_grouped(args) -> int:
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_grouped_fwd
+    from ffn_gated_activation_amd.workloads import GROUPED, grouped_flops, make_grouped_inputs
+    w = GROUPED[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device=dev, seed=0)
+    off = torch.tensor(x["offsets"], dtype=torch.int32, device=dev)
+    out = torch.empty(w.rows, w.inter, dtype=torch.bfloat16, device=dev)
+    gu = torch.empty(w.rows, 2 * w.inter, dtype=torch.bfloat16, device=dev)
+
+    def step(with_gu=False):
+        situ_glu_grouped_fwd(x["x"], x["weight"], off, x["routing_weights"], w.beta, w.linear_beta, out=out,
+                             gate_up_out=gu if with_gu else None)
+
+    def events(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = events(step, args.steps)
+    gu_ms = events(lambda: step(True), max(1, args.steps // 4))
+    kernels = {"grouped_fwd": {"ms": round(k_ms, 5)}, "grouped_fwd_with_gate_up": {"ms": round(gu_ms, 5)}}
+    if args.compare_unfused:
+        # context only: the library grouped GEMM (torch._grouped_mm) writing gate_up, then the
+        # stand-alone activation kernel on it
+        from ffn_gated_activation_amd import situ_glu_fwd
+        wt = x["weight"].transpose(1, 2)
+        ends = off[1:].contiguous()
+        rw2 = x["routing_weights"].reshape(-1, 1)
+
+        def unfused():
+            g = torch._grouped_mm(x["x"], wt, offs=ends)
+            situ_glu_fwd(g, rw2, w.beta, w.linear_beta, out=out)
+        for _ in range(20):
+            unfused()
+        kernels["unfused_grouped_mm_then_activation"] = {"ms": round(events(unfused, 20), 5)}
+    _copy_calibration(args, dev)
+    flops = grouped_flops(args.workload)
+    ms = wall / args.steps * 1e3
+    value = flops / (ms / 1e3) / 1e12
+    achieved = flops / (k_ms / 1e3) / 1e12
+    for k in kernels.values():
+        k["TFLOP/s"] = round(flops / (k["ms"] / 1e3) / 1e12, 2)
+    rec = {
+        "metric": "fused FC1 grouped GEMM + SiTU-GLU achieved TFLOP/s (% of MI355X bf16 dense peak) and rows/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "rows": w.rows, "experts": w.experts,
+                   "hidden": w.hidden, "intermediate": w.inter, "rows_per_expert": x["counts"],
+                   "flops_per_step": flops},
+        "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "rows_per_s": round(w.rows / (ms / 1e3), 1),
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": "situ_glu_grouped_fwd_kernel", "achieved": round(achieved, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic(args.workload, "grouped", GEMM_KERNEL_SOURCE)},
+        "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline_grouped(args.workload,
+                                                                               args.cpu_sample_rows_gemm),
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +309,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=65536,
                     help="rows of the CPU-oracle sample (capped at the workload's rows)")
+    ap.add_argument("--cpu-sample-rows-gemm", type=int, default=65536,
+                    help="rows of the CPU-oracle sample of the grouped GEMM workload")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="grouped GEMM workload: also time torch._grouped_mm + the activation kernel (context)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration runs)")
     args = ap.parse_args(argv)
@@ -205,12 +324,12 @@ def main(argv=None) -> int:
 
     import torch
 
-    from ffn_gated_activation_amd.workloads import ATTN_RES
-    if args.workload in ATTN_RES:
+    from ffn_gated_activation_amd.workloads import ATTN_RES, GROUPED
+    if args.workload in ATTN_RES or args.workload in GROUPED:
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             return 2
-        return bench_attn_res(args)
+        return bench_attn_res(args) if args.workload in ATTN_RES else bench_grouped(args)
 
     from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd, situ_glu_fwd_mxfp8
     from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs

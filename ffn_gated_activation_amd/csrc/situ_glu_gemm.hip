@@ -287,6 +287,10 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
 #define SITU_GEMM_SPLIT 8
 #endif
     constexpr int kFirst = SITU_GEMM_SPLIT;  // loads issued at the boundary, the rest in the next step
+#ifndef SITU_GEMM_SPREAD
+#define SITU_GEMM_SPREAD 2
+#endif
+    constexpr int kSpread = SITU_GEMM_SPREAD;  // products between consecutive loads
     // k steps 0..2 of a stage: products of step kk, fragments of step kk + 1
     // (and the remaining loads of stage kt_next into the other buffer)
     auto first_steps = [&](auto buf, int kt_next) {
@@ -297,12 +301,13 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
         mfmas(f0);
         if (kFirst < kLoads) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < 16; ++q) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (q % kSpread == 0 && q / kSpread < kLoads - kFirst)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (q < 8)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         } else {
             pattern(true, false);
         }
@@ -329,7 +334,7 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q < kFirst)
+            if (q % kSpread == 0 && q / kSpread < kFirst)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
