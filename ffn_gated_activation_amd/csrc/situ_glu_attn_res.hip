@@ -258,6 +258,82 @@ situ_glu_attn_res_vec_kernel(const void *__restrict__ blocks, const void *__rest
     }
 }
 
+// Row-partial form of the reductions (the streaming kernel): each block's
+// two lane sums are reduced inside every row of 16 lanes only (four DPP
+// butterfly steps; every lane of a row then holds the row's sum), and the
+// first lane of each row writes it to its slot: value v (sums of squares of
+// block v for v < 16, dot products of block v - 16 above) of row q of
+// wavefront w at part[v * kRowStride + 4 w + q].  The cross-row and
+// cross-wavefront sums are left to the softmax step, which reads each
+// value's 4 * nwaves partials as 16-byte vectors (the stride is padded so
+// that the 32 reading lanes fall in distinct banks).  Compared with full
+// wavefront sums this saves four lane reads and three adds per sum.
+constexpr int kRowStride = 4 * kMaxWaves + 4;
+constexpr int kRowPartFloats = 2 * kAresMaxBlocks * kRowStride;
+
+__device__ __forceinline__ float row_sum(float x)
+{
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);  // row_half_mirror
+    x += dpp_f<0x140>(x);  // row_mirror
+    return x;
+}
+
+__device__ __forceinline__ void block_row_partials(float ss, float d, int b, float *part)
+{
+    const float s = row_sum(ss);
+    const float t = row_sum(d);
+    if ((threadIdx.x & 15) == 0) {
+        const int slot = (int)(threadIdx.x >> 4);  // 4 * wavefront + row
+        part[b * kRowStride + slot] = s;
+        part[(kAresMaxBlocks + b) * kRowStride + slot] = t;
+    }
+}
+
+// Softmax over MAXNB blocks of which the first nb are real (straight-line:
+// blocks past nb get probability 0), from the row partials: lane v (< 32)
+// adds value v's partials in a fixed order (four running sums over the
+// wavefronts, then pairwise).  P ends in scalar registers.
+template <int MAXNB>
+__device__ __forceinline__ void block_probs_rows(const float *part, int nwaves, int nb, float inv_h, float eps,
+                                                 float *P)
+{
+    const int lane = threadIdx.x & 63;
+    float tot = 0.0f;
+    if (lane < 2 * kAresMaxBlocks) {
+        const float4 *pv = reinterpret_cast<const float4 *>(part + lane * kRowStride);
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float4 v = pv[w];
+            a0 += v.x;
+            a1 += v.y;
+            a2 += v.z;
+            a3 += v.w;
+        }
+        tot = (a0 + a1) + (a2 + a3);
+    }
+    float l[MAXNB];
+    float lmax = -__builtin_inff();
+#pragma unroll
+    for (int b = 0; b < MAXNB; ++b) {
+        const float ss = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), b));
+        const float dd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), kAresMaxBlocks + b));
+        l[b] = b < nb ? dd * __builtin_amdgcn_rsqf(fmaf(ss, inv_h, eps)) : -__builtin_inff();
+        lmax = fmaxf(lmax, l[b]);
+    }
+    float den = 0.0f;
+#pragma unroll
+    for (int b = 0; b < MAXNB; ++b) {
+        l[b] = __builtin_amdgcn_exp2f((l[b] - lmax) * kLog2e);
+        den += l[b];
+    }
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int b = 0; b < MAXNB; ++b)
+        P[b] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(l[b] * inv)));
+}
+
 // Streaming variant of the 128-bit path for up to MAXNB blocks: one
 // workgroup per CU walks the tokens blockIdx.x, + gridDim.x, ...; while a
 // token is reduced and combined, the next token's values are already in
@@ -285,38 +361,6 @@ __device__ __forceinline__ void ares_load_token(uint4 *xv, const char *blocks, c
     }
 }
 
-// Softmax over MAXNB blocks of which the first nb are real (straight-line:
-// blocks past nb get probability 0).  P ends in scalar registers.
-template <int MAXNB>
-__device__ __forceinline__ void block_probs_all(const float *part, int nwaves, int nb, float inv_h, float eps,
-                                                float *P)
-{
-    const int lane = threadIdx.x & 63;
-    float tot = 0.0f;
-    if (lane < 2 * kAresMaxBlocks)
-        for (int w = 0; w < nwaves; ++w)
-            tot += part[w * 2 * kAresMaxBlocks + lane];
-    float l[MAXNB];
-    float lmax = -__builtin_inff();
-#pragma unroll
-    for (int b = 0; b < MAXNB; ++b) {
-        const float ss = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), b));
-        const float dd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), kAresMaxBlocks + b));
-        l[b] = b < nb ? dd * __builtin_amdgcn_rsqf(fmaf(ss, inv_h, eps)) : -__builtin_inff();
-        lmax = fmaxf(lmax, l[b]);
-    }
-    float den = 0.0f;
-#pragma unroll
-    for (int b = 0; b < MAXNB; ++b) {
-        l[b] = __builtin_amdgcn_exp2f((l[b] - lmax) * kLog2e);
-        den += l[b];
-    }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int b = 0; b < MAXNB; ++b)
-        P[b] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(l[b] * inv)));
-}
-
 // One token: sums, barrier, softmax, combine, store.  Blocks past nb were
 // loaded as zeros, so every loop below runs MAXNB times without branches.
 template <int IO, int OUT, int MAXNB>
@@ -336,7 +380,7 @@ __device__ __forceinline__ void ares_mix_token(const uint4 *xv, const float *c, 
             ss = fmaf(x[e], x[e], ss);
             d = fmaf(x[e], c[e], d);
         }
-        block_partials(ss, d, b, part);
+        block_row_partials(ss, d, b, part);
         // one block's reduction at a time: interleaving all of them would
         // need more registers than the two tokens leave
         __builtin_amdgcn_sched_barrier(0);
@@ -346,7 +390,7 @@ __device__ __forceinline__ void ares_mix_token(const uint4 *xv, const float *c, 
     // above the barrier, every block's fp32 copy would be live at once
     __builtin_amdgcn_sched_barrier(0);
     float P[MAXNB];
-    block_probs_all<MAXNB>(part, nwaves, nb, 1.0f / (float)hidden, eps, P);
+    block_probs_rows<MAXNB>(part, nwaves, nb, 1.0f / (float)hidden, eps, P);
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -373,7 +417,7 @@ situ_glu_attn_res_stream_kernel(const void *__restrict__ blocks, const void *__r
     using T = Io<IO>;
     constexpr int E = T::kPerVec;
     constexpr int WB = WBF16 ? 2 : 4;
-    __shared__ float part[2][kMaxWaves * 2 * kAresMaxBlocks];
+    __shared__ __attribute__((aligned(16))) float part[2][kRowPartFloats];
     const int nwaves = blockDim.x >> 6;
     const uint32_t rowb = (uint32_t)hidden * T::kBytes;
     const char *bl = static_cast<const char *>(blocks);
