@@ -503,14 +503,18 @@ using AresFn = void (*)(const void *, const void *, int, int, int, const void *,
 using AresStreamFn = void (*)(const void *, const void *, int, int, int, const void *, const void *, int64_t, float,
                               void *);
 
-// The streaming kernel in four sizes (blocks rounded up to 4, 6, 8 or 10).
+// The streaming kernel for each block count 1..10 (the loops run exactly nb
+// times: no all-zero blocks).
 constexpr int kAresStreamMaxBlocks = 10;
 #define SITU_ARES_SN(IO, OUT, W) \
-    {situ_glu_attn_res_stream_kernel<IO, OUT, W, 4>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 6>, \
-     situ_glu_attn_res_stream_kernel<IO, OUT, W, 8>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 10>}
+    {situ_glu_attn_res_stream_kernel<IO, OUT, W, 1>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 2>, \
+     situ_glu_attn_res_stream_kernel<IO, OUT, W, 3>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 4>, \
+     situ_glu_attn_res_stream_kernel<IO, OUT, W, 5>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 6>, \
+     situ_glu_attn_res_stream_kernel<IO, OUT, W, 7>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 8>, \
+     situ_glu_attn_res_stream_kernel<IO, OUT, W, 9>, situ_glu_attn_res_stream_kernel<IO, OUT, W, 10>}
 #define SITU_ARES_S(IO, OUT) {SITU_ARES_SN(IO, OUT, false), SITU_ARES_SN(IO, OUT, true)}
-// index: [io][out][w_bf16][(nb - 1) / 2 - 1, at least 0: 4, 6, 8, 10 blocks]
-const AresStreamFn kAresStream[2][2][2][4] = {
+// index: [io][out][w_bf16][nb - 1]
+const AresStreamFn kAresStream[2][2][2][kAresStreamMaxBlocks] = {
     {SITU_ARES_S(IO_F32, IO_F32), SITU_ARES_S(IO_F32, IO_BF16)},
     {SITU_ARES_S(IO_BF16, IO_F32), SITU_ARES_S(IO_BF16, IO_BF16)},
 };
@@ -581,8 +585,7 @@ int launch_attn_res(const AresLaunch &L, void *stream)
         const int nv = L.hidden / (L.io == IO_BF16 ? 8 : 4);
         const int threads = ((nv + 63) / 64) * 64;
         const int64_t grid = L.tokens < cu_count() ? L.tokens : cu_count();
-        const int size = L.nb <= 4 ? 0 : (L.nb - 1) / 2 - 1;   // 4, 6, 8, 10 blocks
-        hipLaunchKernelGGL(kAresStream[L.io][L.out_io][L.w_bf16][size], dim3((unsigned)grid), dim3((unsigned)threads), 0,
+        hipLaunchKernelGGL(kAresStream[L.io][L.out_io][L.w_bf16][L.nb - 1], dim3((unsigned)grid), dim3((unsigned)threads), 0,
                            (hipStream_t)stream, L.blocks, L.prefix, L.m, L.nb, L.hidden, L.norm_w, L.proj_w, L.tokens,
                            L.eps, L.out);
         return (int)hipGetLastError();

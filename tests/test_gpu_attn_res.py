@@ -75,7 +75,7 @@ CASES = [
     (8, 0, 4096, True, torch.bfloat16, torch.bfloat16, torch.bfloat16),       # prefix only: one block
     (8, 1, 64, False, torch.float32, torch.float32, torch.float32),           # one stacked block
     (700, 8, 2048, True, torch.bfloat16, torch.bfloat16, torch.bfloat16),     # streaming: 2 or 3 tokens per workgroup
-    (513, 4, 512, True, torch.bfloat16, torch.float32, torch.bfloat16),       # streaming, 5 blocks (6-block kernel)
+    (513, 4, 512, True, torch.bfloat16, torch.float32, torch.bfloat16),       # streaming, 5 blocks
 ]
 
 
@@ -83,6 +83,13 @@ CASES = [
 def test_small(T, m, H, prefix, dt, wdt, odt):
     x = _inputs(T, m, H, prefix, dt, wdt, seed=T + m)
     _check(x, odt, tag=f"T{T} m{m} H{H}")
+
+
+@pytest.mark.parametrize("nb", range(1, 11))
+def test_stream_every_block_count(nb):
+    # the streaming kernel has one instantiation per block count 1..10
+    x = _inputs(300, nb - 1, 1024, True, torch.bfloat16, torch.bfloat16, seed=40 + nb)
+    _check(x, torch.bfloat16, tag=f"stream nb={nb}")
 
 
 def test_eps_zero_and_large():
