@@ -67,22 +67,17 @@ constexpr int kEpiBytes = kBM * kYRowBytes;         // one staged [kBM, kBN] bf1
 static_assert(kBK % 16 == 0 && kCh * kRowsPerBank == 16, "the swizzle assumes 16 rows per bank cycle");
 static_assert(kLoads == 2 * kCh, "x and w rows split evenly over the loads");
 constexpr int kBufBytes = kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes;
-#ifndef SITU_GEMM_GROUP_M
-#define SITU_GEMM_GROUP_M 16
-#endif
-constexpr int kGroupM = SITU_GEMM_GROUP_M;          // row tiles of a super tile
+constexpr int kGroupM = 16;            // row tiles of a super tile (column tiles not a multiple of 16)
+constexpr int kXcdRows = 8;            // row tiles of an XCD's block in the XCD-aware order (x 4 columns)
+constexpr int kFirstLoads = 8;         // of a stage's 16 loads per thread: issued at the boundary, the rest
+                                       // during the next k step
+constexpr int kLoadSpacing = 2;        // products between consecutive loads
 
 using lds_ptr_t = __attribute__((address_space(3))) void *;
 
-// chunk slot of logical chunk c in row r
+// the swizzle of row r: logical chunk c of the row sits in slot c ^ swz(r)
 __device__ __forceinline__ int swz(int r) { return (r / kRowsPerBank) % kCh; }
 
-#ifndef SITU_GEMM_XCD
-#define SITU_GEMM_XCD 1
-#endif
-#ifndef SITU_GEMM_XCD_ROWS
-#define SITU_GEMM_XCD_ROWS 8
-#endif
 // Tile (slot, column tile) of workgroup b.  Workgroups are dealt to the 8
 // XCDs round robin (b % 8), each XCD with its own L2, and 256 (one per CU)
 // run at a time.  With the column tiles a multiple of 16, one such wave of
@@ -94,12 +89,12 @@ __device__ __forceinline__ int swz(int r) { return (r / kRowsPerBank) % kCh; }
 // for a workgroup past the grid's real tiles.
 __device__ __forceinline__ bool tile_of(int b, int slots, int ntn, int &rt, int &ct)
 {
-    if (SITU_GEMM_XCD && ntn % 16 == 0) {
+    if (ntn % 16 == 0) {
         const int x = b & 7, k = b >> 3;
         const int round = k >> 5, q = k & 31;
         const int scols = ntn >> 4;
         const int sr = round / scols, sc = round - sr * scols;
-        constexpr int XR = SITU_GEMM_XCD_ROWS, XC = 32 / XR, NR = 16 / XR;
+        constexpr int XR = kXcdRows, XC = 32 / XR, NR = 16 / XR;
         rt = sr * 16 + (x % NR) * XR + q % XR;
         ct = sc * 16 + (x / NR) * XC + q / XR;
         return rt < slots;
@@ -115,7 +110,7 @@ __device__ __forceinline__ bool tile_of(int b, int slots, int ntn, int &rt, int 
 // Workgroups in the grid: whole super tiles in the XCD mapping.
 __host__ __device__ inline int64_t grid_blocks(int slots, int ntn)
 {
-    if (SITU_GEMM_XCD && ntn % 16 == 0)
+    if (ntn % 16 == 0)
         return (int64_t)((slots + 15) / 16) * 16 * ntn;
     return (int64_t)slots * ntn;
 }
@@ -266,31 +261,20 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
             }
     };
     // Interleave one k step's 16 products with the 8 fragment reads of the
-    // next step (and, optionally, 16 global loads): a read or a pair of loads
-    // between consecutive products keeps LDS and memory requests flowing
-    // while the matrix core works.
-    auto pattern = [](bool reads, bool loads) {
+    // next step: a read between consecutive products keeps LDS requests
+    // flowing while the matrix core works.
+    auto pattern = []() {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // a product
-            if (loads)
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // two global loads
-            if (reads)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     };
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
     Frags f0, f1;
-#ifndef SITU_GEMM_SPLIT
-#define SITU_GEMM_SPLIT 8
-#endif
-    constexpr int kFirst = SITU_GEMM_SPLIT;  // loads issued at the boundary, the rest in the next step
-#ifndef SITU_GEMM_SPREAD
-#define SITU_GEMM_SPREAD 2
-#endif
-    constexpr int kSpread = SITU_GEMM_SPREAD;  // products between consecutive loads
+    constexpr int kFirst = kFirstLoads, kSpread = kLoadSpacing;
     // k steps 0..2 of a stage: products of step kk, fragments of step kk + 1
     // (and the remaining loads of stage kt_next into the other buffer)
     auto first_steps = [&](auto buf, int kt_next) {
@@ -309,14 +293,14 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
         } else {
-            pattern(true, false);
+            pattern();
         }
         read_frags(s, 2, f0);
         mfmas(f1);
-        pattern(true, false);
+        pattern();
         read_frags(s, 3, f1);
         mfmas(f0);
-        pattern(true, false);
+        pattern();
     };
     // the stage boundary: once every wavefront has read its last fragments of
     // the stage in `buf` and its loads of the next stage (other buffer) have
