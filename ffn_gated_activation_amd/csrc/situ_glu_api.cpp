@@ -645,6 +645,9 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
     if (intermediate % 128 || intermediate > SITU_GROUPED_MAX_INTERMEDIATE)
         return fail(SITU_ERR_UNSUPPORTED, "intermediate must be a multiple of 128 up to %d (got %lld)",
                     SITU_GROUPED_MAX_INTERMEDIATE, (long long)intermediate);
+    if (situ::grouped_grid_blocks(rows, experts, intermediate) > (int64_t)0x7fffffff)
+        return fail(SITU_ERR_UNSUPPORTED, "rows %lld, experts %lld and intermediate %lld need more than 2^31 - 1 "
+                    "workgroups", (long long)rows, (long long)experts, (long long)intermediate);
     if (!weight || !group_offsets || !out)
         return fail(SITU_ERR_INVALID_ARG, "weight, group_offsets or out is NULL");
     if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (gate_up_out && !aligned16(gate_up_out)))

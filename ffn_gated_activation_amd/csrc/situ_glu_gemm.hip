@@ -420,14 +420,22 @@ GemmFn pick_gu(bool gu)
 
 }  // namespace
 
-int grouped_slots(int64_t rows, int experts) { return (int)(rows / kBM) + experts; }
+int64_t grouped_slots(int64_t rows, int64_t experts) { return rows / kBM + experts; }
+
+int64_t grouped_grid_blocks(int64_t rows, int64_t experts, int64_t inter)
+{
+    const int64_t slots = grouped_slots(rows, experts), ntn = inter / kBN;
+    return ntn % 16 == 0 ? (slots + 15) / 16 * 16 * ntn : slots * ntn;
+}
 
 int launch_grouped_fwd(const GroupedLaunch &L, void *stream)
 {
-    const int slots = grouped_slots(L.rows, L.experts);
+    const int slots = (int)grouped_slots(L.rows, L.experts);
     const int64_t blocks = grid_blocks(slots, L.inter / kBN);
     if (blocks <= 0)
         return 0;
+    if (blocks > 0x7fffffff)
+        return (int)hipErrorInvalidConfiguration;  // the host API rejects such shapes first
     GemmFn fn = L.lb ? (L.fast ? pick_gu<true, true>(L.gate_up) : pick_gu<true, false>(L.gate_up))
                      : (L.fast ? pick_gu<false, true>(L.gate_up) : pick_gu<false, false>(L.gate_up));
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), L.x, L.w,

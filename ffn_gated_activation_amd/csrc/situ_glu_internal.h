@@ -148,8 +148,10 @@ struct GroupedLaunch {
     GateK gk;
     UpK uk;
 };
-// Row-tile slots of the grouped GEMM grid (floor(rows / 256) + experts).
-int grouped_slots(int64_t rows, int experts);
+// Row-tile slots of the grouped GEMM grid (floor(rows / 256) + experts) and
+// the workgroups of its launch.
+int64_t grouped_slots(int64_t rows, int64_t experts);
+int64_t grouped_grid_blocks(int64_t rows, int64_t experts, int64_t inter);
 
 // Which kernel serves a shape: 0 element path; 1, 3 one 128-bit vector per
 // lane (up to 12 / 16 blocks); 2 two vectors per lane; 4 the streaming kernel.

@@ -299,7 +299,8 @@ int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks,
  * only on that row and its expert's weight, and is bitwise reproducible.
  * Returns SITU_OK, SITU_ERR_INVALID_ARG (bad dtype, beta, count, alignment,
  * NULL pointer, overlap), SITU_ERR_UNSUPPORTED (a dtype other than bf16, a
- * shape outside the limits) or SITU_ERR_DEVICE.
+ * shape outside the limits, or one whose grid of 256-row x 128-column tiles
+ * would exceed 2^31 - 1 workgroups) or SITU_ERR_DEVICE.
  */
 int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows,
                          int64_t hidden, const void *weight, int64_t experts,

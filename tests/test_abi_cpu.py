@@ -220,6 +220,8 @@ def test_grouped_empty_and_unsupported(lib, capi):
     assert _grouped(lib, inter=192) == capi.SITU_ERR_UNSUPPORTED      # not a multiple of 128
     assert _grouped(lib, hidden=capi.SITU_GROUPED_MAX_HIDDEN + 64) == capi.SITU_ERR_UNSUPPORTED
     assert _grouped(lib, rows=1 << 31, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+    # a launch grid beyond 2^31 - 1 workgroups
+    assert _grouped(lib, rows=(1 << 31) - 1, rw_rows=1, inter=1 << 20) == capi.SITU_ERR_UNSUPPORTED
 
 
 def test_grouped_python_layer_rejects():
