@@ -9,7 +9,9 @@ nothing with the HIP library.  This module only compiles them
 with gcc, loads them with ctypes and marshals numpy arrays; the one
 exception is ``grouped_glu_forward`` (FC1 of routed experts followed by the
 activation), whose projections are a numpy float64 matrix product per expert
-feeding the C activation.
+feeding the C activation; ``mx_dequantize`` / ``grouped_glu_forward_mx``
+decode MX block-scaled operands (the C decoder, times 2^(scale - 127) per
+32-value block) before the same products.
 
 Definitions followed (see the header of ``situ_oracle.c``):
   * Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine", section
@@ -415,3 +417,34 @@ def grouped_glu_forward(x, w, m_offsets, rw, beta: float = 4.0, linear_beta=25.0
         res.update(sG=s[:, :inter], sU=s[:, inter:], dY_dG=rr * vgp(g) * tu, dY_dU=rr * tg * vup(u),
                    Tg=tg, Tg_prime=tgp, Tu=tu, Tu_prime=tup, r=np.broadcast_to(rr, (M, inter)))
     return res
+
+
+def mx_dequantize(codes, scales, fmt="e4m3", lib=None) -> np.ndarray:
+    """MX block-scaled values: x = decode(code) * 2^(scale - 127), one scale
+    byte per 32 consecutive values of a row (the last block of a row may be
+    shorter); scale byte 255 (the E8M0 NaN) makes its block NaN."""
+    lib = lib or load()
+    c = np.asarray(codes, dtype=np.uint8)
+    rows, cols = c.shape
+    s = np.asarray(scales, dtype=np.uint8).reshape(rows, -1)
+    assert s.shape[1] == -(-cols // MX_BLOCK)
+    v = fp8_decode_array(c.reshape(-1), fmt, lib=lib).reshape(rows, cols)
+    e = np.repeat(s.astype(np.int64), MX_BLOCK, axis=1)[:, :cols]
+    mult = np.where(e == 255, np.nan, np.ldexp(1.0, (e - 127).clip(-127, 127)))
+    return v * mult
+
+
+def grouped_glu_forward_mx(x_codes, x_scales, w_codes, w_scales, m_offsets, rw, fmt="e4m3", beta: float = 4.0,
+                           linear_beta=25.0, threads: int = 1, want_terms: bool = True, lib=None) -> dict:
+    """The fused FC1 + weighted SiTU-GLU on MX block-scaled operands: x and
+    every expert's weight are decoded (mx_dequantize, scales along the hidden
+    axis) and the products taken exactly (grouped_glu_forward)."""
+    lib = lib or load()
+    xc = np.asarray(x_codes, dtype=np.uint8)
+    wc = np.asarray(w_codes, dtype=np.uint8)
+    E, two_i, K = wc.shape
+    x = mx_dequantize(xc, x_scales, fmt, lib=lib)
+    w = mx_dequantize(wc.reshape(E * two_i, K), np.asarray(w_scales, dtype=np.uint8).reshape(E * two_i, -1), fmt,
+                      lib=lib).reshape(E, two_i, K)
+    return grouped_glu_forward(x, w, m_offsets, rw, beta, linear_beta, threads=threads, want_terms=want_terms,
+                               lib=lib)

@@ -665,4 +665,59 @@ def pin_grouped_glu_brute_force(lib):
         _close(res["dY_dU"][m, j], (f(g, u + h) - f(g, u - h)) / (2 * h), 1e-6, 1e-9, "dY/dU")
 
 
+def pin_mx_dequantize_vs_torch(lib):
+    """MX decoding against torch's float8 dtypes and ldexp written out here:
+    every code of both formats at several scales, ragged last blocks, and the
+    E8M0 NaN scale."""
+    import torch
+    rng = np.random.default_rng(51)
+    for fmt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        codes = rng.integers(0, 256, (3, 70), dtype=np.uint8)
+        if fmt == "e4m3":
+            codes[codes & 0x7F == 0x7F] = 0x11        # keep the NaN codes out of this part
+        else:
+            codes[(codes & 0x7C) == 0x7C] = 0x21      # inf / NaN codes out
+        scales = np.array([[127, 120, 140], [0, 127, 254], [130, 100, 160]], dtype=np.uint8)
+        got = oracle.mx_dequantize(codes, scales, fmt, lib=lib)
+        dec = torch.from_numpy(codes).view(tdt).to(torch.float64).numpy()
+        for r in range(3):
+            for c in range(70):
+                want = dec[r, c] * 2.0 ** (int(scales[r, c // 32]) - 127)
+                assert got[r, c] == want, (fmt, r, c, got[r, c], want)
+    nan = oracle.mx_dequantize(np.full((1, 40), 0x38, np.uint8), np.array([[255, 127]], np.uint8), "e4m3", lib=lib)
+    assert np.all(np.isnan(nan[0, :32])) and np.all(nan[0, 32:] == 1.0)
+
+
+def pin_grouped_mx_brute_force(lib):
+    """The block-scaled grouped forward on a tiny problem against loops that
+    decode every code by the E4M3 definition (sign, 4-bit exponent with bias
+    7, 3-bit mantissa, subnormals at exponent 0) and apply the scales."""
+    rng = np.random.default_rng(53)
+    E, K, I = 2, 64, 2
+    off = [0, 1, 3]
+    xc = rng.integers(0, 0x7F, (3, K), dtype=np.uint8) | (rng.integers(0, 2, (3, K), dtype=np.uint8) << 7)
+    wc = rng.integers(0, 0x7F, (E, 2 * I, K), dtype=np.uint8)
+    xs = rng.integers(120, 135, (3, K // 32), dtype=np.uint8)
+    ws = rng.integers(120, 135, (E, 2 * I, K // 32), dtype=np.uint8)
+    r = rng.uniform(0.2, 1.0, 3)
+
+    def dec(code):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        v = (1 + m / 8) * 2.0 ** (e - 7) if e else (m / 8) * 2.0 ** -6
+        return -v if s else v
+
+    res = oracle.grouped_glu_forward_mx(xc, xs, wc, ws, off, r, "e4m3", 4.0, 25.0, lib=lib)
+    for ex in range(E):
+        for m in range(off[ex], off[ex + 1]):
+            for j in range(I):
+                g = sum(dec(int(xc[m, k])) * 2.0 ** (int(xs[m, k // 32]) - 127) * dec(int(wc[ex, j, k]))
+                        * 2.0 ** (int(ws[ex, j, k // 32]) - 127) for k in range(K))
+                u = sum(dec(int(xc[m, k])) * 2.0 ** (int(xs[m, k // 32]) - 127) * dec(int(wc[ex, I + j, k]))
+                        * 2.0 ** (int(ws[ex, I + j, k // 32]) - 127) for k in range(K))
+                assert abs(res["gate_up"][m, j] - g) <= 1e-13 * max(1.0, abs(g))
+                assert abs(res["gate_up"][m, I + j] - u) <= 1e-13 * max(1.0, abs(u))
+                want = r[m] * oracle.gate(g, 4.0, lib=lib) * oracle.up(u, 25.0, lib=lib)
+                _close(res["out"][m, j], want, 1e-13, 1e-15, "grouped mx out")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -118,14 +118,41 @@ GROUPED_MUTANTS = {
 }
 
 
-def _grouped_mutant(name):
+MXDQ_MUTANTS = {
+    "mx_scale_bias_126": ("np.ldexp(1.0, (e - 127).clip(-127, 127))", "np.ldexp(1.0, (e - 126).clip(-127, 127))"),
+    "mx_block_of_16": ("e = np.repeat(s.astype(np.int64), MX_BLOCK, axis=1)[:, :cols]",
+                       "e = np.repeat(s.astype(np.int64), 16, axis=1)[:, :cols]; e = np.pad(e, ((0, 0), (0, max(0, cols - e.shape[1]))), mode='edge')[:, :cols]"),
+    "mx_scale_ignored": ("return v * mult", "return v"),
+    "mx_nan_scale_ignored": ("mult = np.where(e == 255, np.nan, np.ldexp", "mult = np.where(e == 256, np.nan, np.ldexp"),
+    "mx_scale_negated": ("np.ldexp(1.0, (e - 127).clip(-127, 127))", "np.ldexp(1.0, (127 - e).clip(-127, 127))"),
+}
+
+
+def _py_mutant(func, table, name):
     import inspect
-    old, new = GROUPED_MUTANTS[name]
-    text = inspect.getsource(oracle.grouped_glu_forward)
+    old, new = table[name]
+    text = inspect.getsource(func)
     assert text.count(old) == 1, f"mutation site for {name} not unique/found"
     ns = dict(vars(oracle))
     exec(compile(text.replace(old, new), f"<mutant {name}>", "exec"), ns)
-    return ns["grouped_glu_forward"]
+    return ns[func.__name__]
+
+
+def _grouped_mutant(name):
+    return _py_mutant(oracle.grouped_glu_forward, GROUPED_MUTANTS, name)
+
+
+@pytest.mark.parametrize("name", sorted(MXDQ_MUTANTS))
+def test_mx_dequantize_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "mx_dequantize", _py_mutant(oracle.mx_dequantize, MXDQ_MUTANTS, name))
+    lib = oracle.load()
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(GROUPED_MUTANTS))
