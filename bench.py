@@ -45,6 +45,7 @@ MX_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_mx.hip")
 ARES_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_attn_res.hip")
 GEMM_KERNEL_SOURCE = os.path.join(CSRC, "situ_glu_gemm.hip")
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -191,50 +192,71 @@ def _cpu_baseline_grouped(name: str, sample_rows: int) -> dict:
     import oracle
     from threadpoolctl import threadpool_limits
 
-    from ffn_gated_activation_amd.workloads import GROUPED, make_grouped_inputs
+    from ffn_gated_activation_amd.workloads import GROUPED, GROUPED_MX, make_grouped_inputs, make_grouped_mx_inputs
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     cores = max(1, min(cores, 16))
-    w = GROUPED[name]
-    x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device="cpu", seed=0)
+    mx = name in GROUPED_MX
+    w = GROUPED_MX[name] if mx else GROUPED[name]
+    if mx:
+        x = make_grouped_mx_inputs(w.rows, w.experts, w.hidden, w.inter, "e4m3", device="cpu", seed=0)
+    else:
+        x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device="cpu", seed=0)
     # the first sample_rows rows with their experts' weights (rows are grouped by expert)
     off = x["offsets"]
     n = min(sample_rows, w.rows)
     last = max(e for e in range(w.experts) if off[e] < n)
     sub_off = [min(o, n) for o in off[:last + 2]]
-    xs = x["x"][:n].double().numpy()
-    ws = x["weight"][:last + 1].double().numpy()
     rs = x["routing_weights"][:n].double().numpy()
+    if mx:
+        args = (x["x_codes"][:n].numpy(), x["x_scales"][:n].numpy(), x["weight_codes"][:last + 1].numpy(),
+                x["weight_scales"][:last + 1].numpy())
+    else:
+        args = (x["x"][:n].double().numpy(), x["weight"][:last + 1].double().numpy())
     del x
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
-        oracle.grouped_glu_forward(xs, ws, sub_off, rs, w.beta, w.linear_beta, threads=cores, want_terms=False)
+        if mx:
+            oracle.grouped_glu_forward_mx(*args, sub_off, rs, "e4m3", w.beta, w.linear_beta, threads=cores,
+                                          want_terms=False)
+        else:
+            oracle.grouped_glu_forward(*args, sub_off, rs, w.beta, w.linear_beta, threads=cores, want_terms=False)
         dt = time.perf_counter() - t0
     flops = 2 * n * w.hidden * 2 * w.inter
+    what = "MX decoding + " if mx else ""
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{name} recipe, first {n} rows ({last + 1} expert(s); seed 0, drawn on the host), fp64 "
-                      f"matrix products per expert + fp64 activation, {dt:.2f} s wall",
+            "sample": f"{name} recipe, first {n} rows ({last + 1} expert(s); seed 0, drawn on the host), "
+                      f"{what}fp64 matrix products per expert + fp64 activation, {dt:.2f} s wall",
             "rows_per_s": round(n / dt, 1)}
 
 
 def bench_grouped(args) -> int:
     import torch
 
-    from ffn_gated_activation_amd import situ_glu_grouped_fwd
-    from ffn_gated_activation_amd.workloads import GROUPED, grouped_flops, make_grouped_inputs
-    w = GROUPED[args.workload]
+    from ffn_gated_activation_amd import situ_glu_grouped_fwd, situ_glu_grouped_fwd_mxfp8
+    from ffn_gated_activation_amd.workloads import GROUPED, GROUPED_MX, make_grouped_inputs, make_grouped_mx_inputs
+    mx = args.workload in GROUPED_MX
+    w = GROUPED_MX[args.workload] if mx else GROUPED[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device=dev, seed=0)
+    if mx:
+        x = make_grouped_mx_inputs(w.rows, w.experts, w.hidden, w.inter, "e4m3", device=dev, seed=0)
+    else:
+        x = make_grouped_inputs(w.rows, w.experts, w.hidden, w.inter, device=dev, seed=0)
     off = torch.tensor(x["offsets"], dtype=torch.int32, device=dev)
     out = torch.empty(w.rows, w.inter, dtype=torch.bfloat16, device=dev)
     gu = torch.empty(w.rows, 2 * w.inter, dtype=torch.bfloat16, device=dev)
 
     def step(with_gu=False):
-        situ_glu_grouped_fwd(x["x"], x["weight"], off, x["routing_weights"], w.beta, w.linear_beta, out=out,
-                             gate_up_out=gu if with_gu else None)
+        if mx:
+            situ_glu_grouped_fwd_mxfp8(x["x_codes"], x["x_scales"], x["weight_codes"], x["weight_scales"], off,
+                                       x["routing_weights"], "e4m3", w.beta, w.linear_beta, out=out,
+                                       gate_up_out=gu if with_gu else None)
+        else:
+            situ_glu_grouped_fwd(x["x"], x["weight"], off, x["routing_weights"], w.beta, w.linear_beta, out=out,
+                                 gate_up_out=gu if with_gu else None)
 
     def events(fn, n):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -256,7 +278,7 @@ def bench_grouped(args) -> int:
     k_ms = events(step, args.steps)
     gu_ms = events(lambda: step(True), max(1, args.steps // 4))
     kernels = {"grouped_fwd": {"ms": round(k_ms, 5)}, "grouped_fwd_with_gate_up": {"ms": round(gu_ms, 5)}}
-    if args.compare_unfused:
+    if args.compare_unfused and not mx:
         # context only: the library grouped GEMM (torch._grouped_mm) writing gate_up, then the
         # stand-alone activation kernel on it
         from ffn_gated_activation_amd import situ_glu_fwd
@@ -271,25 +293,27 @@ def bench_grouped(args) -> int:
             unfused()
         kernels["unfused_grouped_mm_then_activation"] = {"ms": round(events(unfused, 20), 5)}
     _copy_calibration(args, dev)
-    flops = grouped_flops(args.workload)
+    flops = 2 * w.rows * w.hidden * 2 * w.inter
+    peak = FP8_PEAK_TFLOPS if mx else BF16_PEAK_TFLOPS
     ms = wall / args.steps * 1e3
     value = flops / (ms / 1e3) / 1e12
     achieved = flops / (k_ms / 1e3) / 1e12
     for k in kernels.values():
         k["TFLOP/s"] = round(flops / (k["ms"] / 1e3) / 1e12, 2)
+    prec = "MXFP8 (E4M3)" if mx else "bf16"
     rec = {
-        "metric": "fused FC1 grouped GEMM + SiTU-GLU achieved TFLOP/s (% of MI355X bf16 dense peak) and rows/s",
+        "metric": f"fused FC1 grouped GEMM + SiTU-GLU achieved TFLOP/s (% of MI355X {prec} dense peak) and rows/s",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "fp8-e4m3-mx" if mx else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rows": w.rows, "experts": w.experts,
                    "hidden": w.hidden, "intermediate": w.inter, "rows_per_expert": x["counts"],
                    "flops_per_step": flops},
-        "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "rows_per_s": round(w.rows / (ms / 1e3), 1),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": "situ_glu_grouped_fwd_kernel", "achieved": round(achieved, 2),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": _traffic(args.workload, "grouped", GEMM_KERNEL_SOURCE)},
         "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline_grouped(args.workload,
                                                                                args.cpu_sample_rows_gemm),
@@ -324,8 +348,8 @@ def main(argv=None) -> int:
 
     import torch
 
-    from ffn_gated_activation_amd.workloads import ATTN_RES, GROUPED
-    if args.workload in ATTN_RES or args.workload in GROUPED:
+    from ffn_gated_activation_amd.workloads import ATTN_RES, GROUPED, GROUPED_MX
+    if args.workload in ATTN_RES or args.workload in GROUPED or args.workload in GROUPED_MX:
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             return 2

@@ -620,15 +620,22 @@ int situ_glu_attn_res_fwd(const void *blocks, int64_t tokens, int64_t nblocks, i
     return SITU_OK;
 }
 
-int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidden, const void *weight,
-                         int64_t experts, int64_t intermediate, const int32_t *group_offsets,
-                         const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
-                         const double *linear_beta, void *out, void *gate_up_out, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of the fused grouped forward.  op 0: bf16 x
+// and weight; 1 / 2: MX E4M3 / E5M2 codes with scale bytes (one per 32
+// values along the hidden axis).
+int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64_t hidden, const void *weight,
+                const void *w_scales, int64_t experts, int64_t intermediate, const int32_t *group_offsets,
+                const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta, const double *linear_beta,
+                void *out, void *gate_up_out, void *stream)
 {
-    g_last_error.clear();
-    if (io_dtype != SITU_DTYPE_BF16)
-        return fail(SITU_ERR_UNSUPPORTED, "the grouped GEMM takes bf16 x and weight only (io_dtype %d)", io_dtype);
-    int rc = check_common(x, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows, beta, linear_beta);
+    const int64_t kstep = op ? 128 : 64;     // hidden elements of one pipeline stage
+    const int64_t es = op ? 1 : 2;           // bytes per operand element
+    int rc = check_common(x, SITU_DTYPE_BF16, rows, intermediate, routing_weights, rw_dtype, rw_rows, beta,
+                          linear_beta);
     if (rc)
         return rc;
     if (hidden < 0 || experts < 0)
@@ -639,9 +646,9 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
     if (experts < 1 || experts > SITU_GROUPED_MAX_EXPERTS)
         return fail(SITU_ERR_INVALID_ARG, "experts must be 1 to %d (got %lld)", SITU_GROUPED_MAX_EXPERTS,
                     (long long)experts);
-    if (hidden < 64 || hidden % 64 || hidden > SITU_GROUPED_MAX_HIDDEN)
-        return fail(SITU_ERR_UNSUPPORTED, "hidden must be a positive multiple of 64 up to %d (got %lld)",
-                    SITU_GROUPED_MAX_HIDDEN, (long long)hidden);
+    if (hidden < kstep || hidden % kstep || hidden > SITU_GROUPED_MAX_HIDDEN)
+        return fail(SITU_ERR_UNSUPPORTED, "hidden must be a positive multiple of %lld up to %d (got %lld)",
+                    (long long)kstep, SITU_GROUPED_MAX_HIDDEN, (long long)hidden);
     if (intermediate % 128 || intermediate > SITU_GROUPED_MAX_INTERMEDIATE)
         return fail(SITU_ERR_UNSUPPORTED, "intermediate must be a multiple of 128 up to %d (got %lld)",
                     SITU_GROUPED_MAX_INTERMEDIATE, (long long)intermediate);
@@ -650,13 +657,21 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
                     "workgroups", (long long)rows, (long long)experts, (long long)intermediate);
     if (!weight || !group_offsets || !out)
         return fail(SITU_ERR_INVALID_ARG, "weight, group_offsets or out is NULL");
+    if (op && (!x_scales || !w_scales))
+        return fail(SITU_ERR_INVALID_ARG, "x_scales or w_scales is NULL");
     if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (gate_up_out && !aligned16(gate_up_out)))
         return fail(SITU_ERR_INVALID_ARG, "x, weight, out and gate_up_out must be 16-byte aligned");
+    if (op && (!aligned_to(x_scales, 4) || !aligned_to(w_scales, 4)))
+        return fail(SITU_ERR_INVALID_ARG, "x_scales and w_scales must be 4-byte aligned");
     if (!aligned_to(group_offsets, 4))
         return fail(SITU_ERR_INVALID_ARG, "group_offsets is not 4-byte aligned");
+    const int64_t sb = hidden / 32;
     const Range outs[] = {range("out", out, rows * intermediate * 2),
                           range("gate_up_out", gate_up_out, gate_up_out ? rows * intermediate * 4 : 0)};
-    const Range ins[] = {range("x", x, rows * hidden * 2), range("weight", weight, experts * 2 * intermediate * hidden * 2),
+    const Range ins[] = {range("x", x, rows * hidden * es),
+                         range("weight", weight, experts * 2 * intermediate * hidden * es),
+                         range("x_scales", x_scales, op ? rows * sb : 0),
+                         range("w_scales", w_scales, op ? experts * 2 * intermediate * sb : 0),
                          range("group_offsets", group_offsets, (experts + 1) * 4),
                          range("routing_weights", routing_weights, rw_rows * dtype_bytes(rw_dtype))};
     for (const Range &o : outs)
@@ -667,8 +682,11 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
         return fail(SITU_ERR_INVALID_ARG, "out overlaps gate_up_out");
 
     situ::GroupedLaunch L{};
+    L.op = op;
     L.x = x;
     L.w = weight;
+    L.x_scales = x_scales;
+    L.w_scales = w_scales;
     L.offsets = group_offsets;
     L.rows = rows;
     L.hidden = (int)hidden;
@@ -687,6 +705,37 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
     if (err)
         return fail(SITU_ERR_DEVICE, "grouped GEMM launch failed: %s", situ::device_error_string(err));
     return SITU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidden, const void *weight,
+                         int64_t experts, int64_t intermediate, const int32_t *group_offsets,
+                         const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                         const double *linear_beta, void *out, void *gate_up_out, void *stream)
+{
+    g_last_error.clear();
+    if (io_dtype != SITU_DTYPE_BF16)
+        return fail(SITU_ERR_UNSUPPORTED, "the grouped GEMM takes bf16 x and weight only (io_dtype %d)", io_dtype);
+    return grouped_fwd(0, x, nullptr, rows, hidden, weight, nullptr, experts, intermediate, group_offsets,
+                       routing_weights, rw_dtype, rw_rows, beta, linear_beta, out, gate_up_out, stream);
+}
+
+int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales, int64_t rows, int64_t hidden,
+                               const void *w_codes, const void *w_scales, int64_t experts, int64_t intermediate,
+                               int fp8_format, const int32_t *group_offsets, const void *routing_weights,
+                               int rw_dtype, int64_t rw_rows, double beta, const double *linear_beta, void *out,
+                               void *gate_up_out, void *stream)
+{
+    g_last_error.clear();
+    if (fp8_format != SITU_FP8_E4M3 && fp8_format != SITU_FP8_E5M2)
+        return fail(SITU_ERR_INVALID_ARG, "fp8_format %d is not SITU_FP8_E4M3 (0) or SITU_FP8_E5M2 (1)",
+                    fp8_format);
+    return grouped_fwd(fp8_format == SITU_FP8_E4M3 ? 1 : 2, x_codes, x_scales, rows, hidden, w_codes, w_scales,
+                       experts, intermediate, group_offsets, routing_weights, rw_dtype, rw_rows, beta, linear_beta,
+                       out, gate_up_out, stream);
 }
 
 }  // extern "C"

@@ -50,10 +50,15 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Operand kinds: bf16, or MX block-scaled fp8 (E4M3 / E5M2 codes with one
+// E8M0 scale byte per 32 values along the hidden axis).
+enum { OP_BF16 = 0, OP_E4M3 = 1, OP_E5M2 = 2 };
 
 constexpr int kBM = 256;               // rows of a tile
 constexpr int kBN = 128;               // output columns of a tile
-constexpr int kBK = 64;                // hidden elements per stage (two stage buffers)
+constexpr int kBK = 64;                // bf16 hidden elements per stage (two stage buffers)
 constexpr int kThreads = 256;
 constexpr int kCh = kBK / 8;                        // 16-byte chunks of a row in one stage
 constexpr int kRowB = kBK * 2;                      // bytes of a row in one stage
@@ -129,18 +134,29 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool LB, bool FAST, bool GU>
+template <int OP, bool LB, bool FAST, bool GU>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__ w,
+                            const uint8_t *__restrict__ xs, const uint8_t *__restrict__ ws,
                             const int32_t *__restrict__ offsets, int64_t rows, int hidden, int experts,
                             int inter, int slots, const void *__restrict__ rw, int rw_bf16, int64_t rw_stride,
                             void *__restrict__ out, void *__restrict__ gate_up, GateK gk, UpK uk)
 {
+    // bf16: 64 hidden elements per 128-byte stage row, four 16-wide k steps;
+    // fp8: 128 per row, two 64-wide k steps of scaled products
+    constexpr bool F8 = OP != OP_BF16;
+    constexpr int kStageK = F8 ? 128 : kBK;
+    constexpr int kSteps = F8 ? 2 : 4;
+    constexpr int kFragReads = F8 ? 16 : 8;  // LDS reads of one k step's fragments
     // Two stage buffers as two objects: the compiler then knows that loads
     // landing in one do not alias the fragment reads of the other, and does
     // not make those reads wait for the loads in flight.
     __shared__ __attribute__((aligned(1024))) char smem0[kBufBytes];
     __shared__ __attribute__((aligned(1024))) char smem1[kBufBytes];
+    // fp8: the stage's scale bytes, one dword (4 blocks of 32) per x row (0..255)
+    // and per gate / up row (256..511), per buffer
+    __shared__ __attribute__((aligned(16))) uint32_t ssc0[F8 ? 2 * kBM : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t ssc1[F8 ? 2 * kBM : 1];
     __shared__ float s_rs[kBM];
     __shared__ int s_expert;
 
@@ -183,7 +199,7 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     // ---- operand descriptors.  Loads of rows 0..kBM-1 of one region: x rows
     // of the tile (past nrows they read as zero), gate rows 0..kBN-1 and, via
     // a base kBN rows early, up rows kBN..2kBN-1 of the same offsets.
-    const uint32_t kbytes = (uint32_t)hidden * 2u;
+    const uint32_t kbytes = (uint32_t)hidden * (F8 ? 1u : 2u);
     const char *xb = static_cast<const char *>(x) + (int64_t)row0 * kbytes;
     const char *wb = static_cast<const char *>(w) + ((int64_t)e * 2 * inter + n0) * kbytes;
     const rsrc_t ra = make_rsrc(xb, (uint32_t)nrows * kbytes);
@@ -202,8 +218,29 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
         const int r = (4 * j + wv) * kRowsPerLoad + lane / kCh;
         voff[j] = (uint32_t)r * kbytes + (uint32_t)(((lane % kCh) ^ swz(r)) * 16);
     }
-    const int nk = hidden / kBK;
+    const int nk = hidden / kStageK;
     const rsrc_t rz = make_rsrc(xb, 0u);  // reads as zero: the padding stage of an odd count
+    // fp8 scales: row r's bytes for stage kt are the dword at r * (K / 32) + 4 kt
+    const uint32_t sbytes = (uint32_t)hidden / 32u;
+    rsrc_t rsa = rz, rsg = rz, rsu = rz;
+    if (F8) {
+        rsa = make_rsrc(xs + (int64_t)row0 * sbytes, (uint32_t)nrows * sbytes);
+        const uint8_t *wsb = ws + ((int64_t)e * 2 * inter + n0) * sbytes;
+        rsg = make_rsrc(wsb, (uint32_t)kBN * sbytes);
+        rsu = make_rsrc(wsb + ((int64_t)inter - kBN) * sbytes, (uint32_t)(2 * kBN) * sbytes);
+    }
+    // wavefront wv loads the scale dwords of x rows and of w rows 64 wv..64 wv + 63
+    auto issue_scales = [&](int kt, auto buf) {
+        if (!F8)
+            return;
+        uint32_t *base = decltype(buf)::value ? ssc1 : ssc0;
+        const bool live = kt < nk;
+        const uint32_t vo = (uint32_t)(64 * wv + lane) * sbytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rz, (lds_ptr_t)(base + 64 * wv), 4, (int)vo,
+                                                 kt * 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? (wv < 2 ? rsg : rsu) : rz,
+                                                 (lds_ptr_t)(base + kBM + 64 * wv), 4, (int)vo, kt * 4, 0, 0);
+    };
     auto issue = [&](int kt, auto buf, int j0 = 0, int j1 = kLoads) {
         const uint32_t so = (uint32_t)kt * kRowB;
         char *base = decltype(buf)::value ? smem1 : smem0;
@@ -221,13 +258,22 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     const int wm = wv >> 1, wn = wv & 1;
     const int l32 = lane & 31, lh = lane >> 5;
     const int f = swz(l32);  // the swizzle of every row this lane reads (row bases are multiples of 32)
-    uint32_t rda[kBK / 16], rdb[kBK / 16];
+    // fragment addresses of each k step.  bf16: 16 bytes at logical chunk
+    // 2 kk + lh.  fp8: two 16-byte pieces at chunks 4 s + lh and 4 s + 2 + lh,
+    // which the scaled product takes as its 32 bytes in the order k =
+    // 16 c + 8 lh + (0..7) (c = 8-byte piece): a consistent permutation of
+    // the 64 k of the step for both operands that keeps each 32-wide scale
+    // block (hardware k 0..31 = this step's first MX block) whole
+    uint32_t rda[kSteps][F8 ? 2 : 1], rdb[kSteps][F8 ? 2 : 1];
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-        const uint32_t c = (uint32_t)(((2 * kk + lh) ^ f) * 16);
-        rda[kk] = (uint32_t)(wm * 128 + l32) * kRowB + c;
-        rdb[kk] = (uint32_t)(kARows + wn * 64 + l32) * kRowB + c;
-    }
+    for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int h = 0; h < (F8 ? 2 : 1); ++h) {
+            const int chunk = F8 ? 4 * st + 2 * h + lh : 2 * st + lh;
+            const uint32_t c = (uint32_t)((chunk ^ f) * 16);
+            rda[st][h] = (uint32_t)(wm * 128 + l32) * kRowB + c;
+            rdb[st][h] = (uint32_t)(kARows + wn * 64 + l32) * kRowB + c;
+        }
 
     f32x16 accg[4][2], accu[4][2];
 #pragma unroll
@@ -238,87 +284,128 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
             accu[i][j] = f32x16{};
         }
 
+    using FragT = typename std::conditional<F8, i32x8, bf16x8>::type;
     struct Frags {
-        bf16x8 a[4], g[2], u[2];
+        FragT a[4], g[2], u[2];
     };
-    auto read_frags = [&](const char *s, int kk, Frags &f) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f.a[i] = *reinterpret_cast<const bf16x8 *>(s + rda[kk] + i * 32 * kRowB);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            f.g[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + j * 32 * kRowB);
-            f.u[j] = *reinterpret_cast<const bf16x8 *>(s + rdb[kk] + (kBN + j * 32) * kRowB);
+    auto frag = [&](const char *s, uint32_t r0, uint32_t r1, int off) -> FragT {
+        if constexpr (F8) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(s + r0 + off);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(s + r1 + off);
+            return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+            return *reinterpret_cast<const bf16x8 *>(s + r0 + off);
         }
     };
-    auto mfmas = [&](const Frags &f) {
+    auto read_frags = [&](const char *s, int st, Frags &fr) {
+        const uint32_t a0 = rda[st][0], a1 = rda[st][F8 ? 1 : 0];
+        const uint32_t b0 = rdb[st][0], b1 = rdb[st][F8 ? 1 : 0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fr.a[i] = frag(s, a0, a1, i * 32 * kRowB);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            fr.g[j] = frag(s, b0, b1, j * 32 * kRowB);
+            fr.u[j] = frag(s, b0, b1, (kBN + j * 32) * kRowB);
+        }
+    };
+    // fp8: scale dwords of the rows this lane feeds (x rows of a[i], weight
+    // rows of g[j] / u[j]); byte 2 st + lh is the scale of step st's block lh
+    struct Scales {
+        uint32_t a[4], g[2], u[2];
+    };
+    auto read_scales = [&](const uint32_t *sc, Scales &q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q.a[i] = sc[wm * 128 + i * 32 + l32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            q.g[j] = sc[kBM + wn * 64 + j * 32 + l32];
+            q.u[j] = sc[kBM + kBN + wn * 64 + j * 32 + l32];
+        }
+    };
+    constexpr int kCbsz = OP == OP_E5M2 ? 1 : 0;  // operand format of the scaled product (same for both)
+    auto mfmas = [&](const Frags &fr, const Scales &q, int st) {
+        const uint32_t sh = (uint32_t)(8 * (2 * st + lh));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.g[j], accg[i][j], 0, 0, 0);
-                accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.u[j], accu[i][j], 0, 0, 0);
+                if constexpr (F8) {
+                    const int sa = (int)(q.a[i] >> sh);
+                    accg[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fr.a[i], fr.g[j], accg[i][j], kCbsz, kCbsz, 0, sa, 0, (int)(q.g[j] >> sh));
+                    accu[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fr.a[i], fr.u[j], accu[i][j], kCbsz, kCbsz, 0, sa, 0, (int)(q.u[j] >> sh));
+                } else {
+                    accg[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.g[j], accg[i][j], 0, 0, 0);
+                    accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.u[j], accu[i][j], 0, 0, 0);
+                }
             }
     };
-    // Interleave one k step's 16 products with the 8 fragment reads of the
+    // Interleave one k step's 16 products with the fragment reads of the
     // next step: a read between consecutive products keeps LDS requests
     // flowing while the matrix core works.
     auto pattern = []() {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < kFragReads; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        if (kFragReads < 16)
+            __builtin_amdgcn_sched_group_barrier(0x008, 16 - kFragReads, 0);
     };
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
     Frags f0, f1;
+    Scales q0, q1;  // scales of the stage in buffer 0 / buffer 1 (fp8)
     constexpr int kFirst = kFirstLoads, kSpread = kLoadSpacing;
-    // k steps 0..2 of a stage: products of step kk, fragments of step kk + 1
-    // (and the remaining loads of stage kt_next into the other buffer)
+    // k steps 0..kSteps-2 of a stage: products of step st, fragments of step
+    // st + 1 (and the remaining loads of stage kt_next into the other buffer)
     auto first_steps = [&](auto buf, int kt_next) {
         const char *s = decltype(buf)::value ? smem1 : smem0;
+        const Scales &q = decltype(buf)::value ? q1 : q0;
         read_frags(s, 1, f1);
-        if (kFirst < kLoads)
-            issue(kt_next, std::integral_constant<int, 1 - decltype(buf)::value>{}, kFirst, kLoads);
-        mfmas(f0);
-        if (kFirst < kLoads) {
+        issue(kt_next, std::integral_constant<int, 1 - decltype(buf)::value>{}, kFirst, kLoads);
+        mfmas(f0, q, 0);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (q % kSpread == 0 && q / kSpread < kLoads - kFirst)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                if (q < 8)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-        } else {
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i % kSpread == 0 && i / kSpread < kLoads - kFirst)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (i < kFragReads)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (!F8) {
+            read_frags(s, 2, f0);
+            mfmas(f1, q, 1);
+            pattern();
+            read_frags(s, 3, f1);
+            mfmas(f0, q, 2);
             pattern();
         }
-        read_frags(s, 2, f0);
-        mfmas(f1);
-        pattern();
-        read_frags(s, 3, f1);
-        mfmas(f0);
-        pattern();
     };
     // the stage boundary: once every wavefront has read its last fragments of
     // the stage in `buf` and its loads of the next stage (other buffer) have
-    // landed, one barrier; then the next stage's first fragments and the
-    // loads of stage kt_next (into `buf`) go out while the last 16 products
-    // of the stage run
+    // landed, one barrier; then the next stage's first fragments (and
+    // scales) and the loads of stage kt_next (into `buf`) go out while the
+    // last 16 products of the stage run
     auto boundary = [&](auto buf, int kt_next) {
         constexpr int nb = 1 - decltype(buf)::value;
+        const Scales &q = decltype(buf)::value ? q1 : q0;
         wait_vmcnt<0>();
         __syncthreads();
         read_frags(nb ? smem1 : smem0, 0, f0);
+        if (F8)
+            read_scales(nb ? ssc1 : ssc0, nb ? q1 : q0);
+        issue_scales(kt_next, buf);
         issue(kt_next, buf, 0, kFirst);
-        mfmas(f1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        mfmas(f1, q, kSteps - 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, F8 ? kFragReads + 8 : kFragReads, 0);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q % kSpread == 0 && q / kSpread < kFirst)
+            if (i % kSpread == 0 && i / kSpread < kFirst + (F8 ? 2 : 0))
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -328,12 +415,15 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     // kt + 1 are in flight while stage kt is multiplied.  The body is two
     // stages (one per buffer) with no tail: an odd stage count gets one more
     // stage of zeros (an empty descriptor), which adds nothing.
+    issue_scales(0, Buf0{});
     issue(0, Buf0{});
     wait_vmcnt<0>();
     __syncthreads();
     read_frags(smem0, 0, f0);
+    if (F8)
+        read_scales(ssc0, q0);
+    issue_scales(1, Buf1{});
     issue(1, Buf1{}, 0, kFirst);
-    // (the second half of stage 1's loads: issued with stage 0's first step)
     for (int kt = 0; kt < nk; kt += 2) {
         first_steps(Buf0{}, kt + 1);
         boundary(Buf0{}, kt + 2);
@@ -409,13 +499,20 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     }
 }
 
-using GemmFn = void (*)(const void *, const void *, const int32_t *, int64_t, int, int, int, int, const void *,
-                        int, int64_t, void *, void *, GateK, UpK);
+using GemmFn = void (*)(const void *, const void *, const uint8_t *, const uint8_t *, const int32_t *, int64_t, int,
+                        int, int, int, const void *, int, int64_t, void *, void *, GateK, UpK);
 
-template <bool LB, bool FAST>
+template <int OP, bool LB, bool FAST>
 GemmFn pick_gu(bool gu)
 {
-    return gu ? situ_glu_grouped_fwd_kernel<LB, FAST, true> : situ_glu_grouped_fwd_kernel<LB, FAST, false>;
+    return gu ? situ_glu_grouped_fwd_kernel<OP, LB, FAST, true> : situ_glu_grouped_fwd_kernel<OP, LB, FAST, false>;
+}
+
+template <int OP>
+GemmFn pick(bool lb, bool fast, bool gu)
+{
+    return lb ? (fast ? pick_gu<OP, true, true>(gu) : pick_gu<OP, true, false>(gu))
+              : (fast ? pick_gu<OP, false, true>(gu) : pick_gu<OP, false, false>(gu));
 }
 
 }  // namespace
@@ -436,11 +533,14 @@ int launch_grouped_fwd(const GroupedLaunch &L, void *stream)
         return 0;
     if (blocks > 0x7fffffff)
         return (int)hipErrorInvalidConfiguration;  // the host API rejects such shapes first
-    GemmFn fn = L.lb ? (L.fast ? pick_gu<true, true>(L.gate_up) : pick_gu<true, false>(L.gate_up))
-                     : (L.fast ? pick_gu<false, true>(L.gate_up) : pick_gu<false, false>(L.gate_up));
+    const bool gu = L.gate_up != nullptr;
+    const GemmFn fn = L.op == OP_E4M3 ? pick<OP_E4M3>(L.lb, L.fast, gu)
+                      : L.op == OP_E5M2 ? pick<OP_E5M2>(L.lb, L.fast, gu)
+                                        : pick<OP_BF16>(L.lb, L.fast, gu);
     hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), L.x, L.w,
-                       L.offsets, L.rows, L.hidden, L.experts, L.inter, slots, L.rw, L.rw_bf16, L.rw_stride, L.out,
-                       L.gate_up, L.gk, L.uk);
+                       static_cast<const uint8_t *>(L.x_scales), static_cast<const uint8_t *>(L.w_scales), L.offsets,
+                       L.rows, L.hidden, L.experts, L.inter, slots, L.rw, L.rw_bf16, L.rw_stride, L.out, L.gate_up,
+                       L.gk, L.uk);
     return (int)hipGetLastError();
 }
 

@@ -127,12 +127,17 @@ struct AresLaunch {
     int out_io;           // output dtype
     int vec;              // 16-byte aligned buffers, rows a whole number of 128-bit vectors
 };
-// Fused FC1 grouped GEMM + SiTU-GLU (bf16): x [rows, hidden], w [experts,
-// 2 inter, hidden], offsets [experts + 1] int32 in device memory; hidden a
-// multiple of 64, inter a multiple of 128, all 16-byte aligned.
+// Fused FC1 grouped GEMM + SiTU-GLU: x [rows, hidden], w [experts,
+// 2 inter, hidden], offsets [experts + 1] int32 in device memory; bf16
+// operands (hidden a multiple of 64) or MX fp8 codes with scale bytes
+// [rows, hidden / 32] and [experts, 2 inter, hidden / 32] (hidden a multiple
+// of 128); inter a multiple of 128; operands 16-byte aligned.
 struct GroupedLaunch {
+    int op;               // 0 bf16, 1 MX E4M3, 2 MX E5M2
     const void *x;
     const void *w;
+    const void *x_scales;
+    const void *w_scales;
     const int32_t *offsets;
     int64_t rows;
     int hidden;

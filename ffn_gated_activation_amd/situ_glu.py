@@ -258,6 +258,27 @@ def apply_attn_res(prefix_sum: torch.Tensor, block_residual: torch.Tensor, norm_
                                  proj_weight, eps, out_dtype)
 
 
+def _grouped_outputs(rows, experts, two_i, group_offsets, routing_weights, out, want_gate_up, gate_up_out,
+                     device):
+    inter = two_i // 2
+    if group_offsets.dtype != torch.int32 or group_offsets.numel() != experts + 1 or not group_offsets.is_contiguous():
+        raise ValueError(f"group_offsets must be a contiguous int32 tensor of {experts + 1} values")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    rw_rows = routing_weights.numel()
+    if rw_rows not in (rows, 1) or not routing_weights.is_contiguous():
+        raise ValueError(f"routing_weights must hold {rows} row-aligned values or one weight")
+    if out is None:
+        out = torch.empty(rows, inter, dtype=torch.bfloat16, device=device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, inter) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{rows}, {inter}] bfloat16 tensor")
+    if want_gate_up and gate_up_out is None:
+        gate_up_out = torch.empty(rows, two_i, dtype=torch.bfloat16, device=device)
+    if gate_up_out is not None and (gate_up_out.dtype != torch.bfloat16 or tuple(gate_up_out.shape) != (rows, two_i)
+                                    or not gate_up_out.is_contiguous()):
+        raise ValueError(f"gate_up_out must be a contiguous [{rows}, {two_i}] bfloat16 tensor")
+    return rwd, rw_rows, out, gate_up_out
+
+
 def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: torch.Tensor,
                          routing_weights: torch.Tensor, beta: float = 4.0, linear_beta: float | None = 25.0,
                          want_gate_up: bool = False, out: torch.Tensor | None = None,
@@ -279,26 +300,57 @@ def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: t
     experts, two_i, k2 = weight.shape
     if k2 != hidden or two_i % 2:
         raise ValueError(f"weight must be [E, 2I, {hidden}], got {tuple(weight.shape)}")
-    inter = two_i // 2
-    if group_offsets.dtype != torch.int32 or group_offsets.numel() != experts + 1 or not group_offsets.is_contiguous():
-        raise ValueError(f"group_offsets must be a contiguous int32 tensor of {experts + 1} values")
-    rwd = _io_dtype(routing_weights, "routing_weights")
-    rw_rows = routing_weights.numel()
-    if rw_rows not in (rows, 1) or not routing_weights.is_contiguous():
-        raise ValueError(f"routing_weights must hold {rows} row-aligned values or one weight")
-    if out is None:
-        out = torch.empty(rows, inter, dtype=torch.bfloat16, device=x.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, inter) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous [{rows}, {inter}] bfloat16 tensor")
-    if want_gate_up and gate_up_out is None:
-        gate_up_out = torch.empty(rows, two_i, dtype=torch.bfloat16, device=x.device)
-    if gate_up_out is not None and (gate_up_out.dtype != torch.bfloat16 or tuple(gate_up_out.shape) != (rows, two_i)
-                                    or not gate_up_out.is_contiguous()):
-        raise ValueError(f"gate_up_out must be a contiguous [{rows}, {two_i}] bfloat16 tensor")
+    rwd, rw_rows, out, gate_up_out = _grouped_outputs(rows, experts, two_i, group_offsets, routing_weights, out,
+                                                      want_gate_up, gate_up_out, x.device)
     _capi.check(lib.situ_glu_grouped_fwd(
-        x.data_ptr(), _capi.SITU_DTYPE_BF16, rows, hidden, weight.data_ptr(), experts, inter,
+        x.data_ptr(), _capi.SITU_DTYPE_BF16, rows, hidden, weight.data_ptr(), experts, two_i // 2,
         group_offsets.data_ptr(), routing_weights.data_ptr(), rwd, rw_rows, float(beta), _capi.lb_ptr(linear_beta),
         out.data_ptr(), gate_up_out.data_ptr() if gate_up_out is not None else None, _stream()), lib)
+    return (out, gate_up_out) if gate_up_out is not None else out
+
+
+_FP8_CODE_DTYPES = {"e4m3": (torch.uint8, torch.float8_e4m3fn), "e5m2": (torch.uint8, torch.float8_e5m2)}
+
+
+def situ_glu_grouped_fwd_mxfp8(x_codes: torch.Tensor, x_scales: torch.Tensor, weight_codes: torch.Tensor,
+                               weight_scales: torch.Tensor, group_offsets: torch.Tensor,
+                               routing_weights: torch.Tensor, fp8_format: str = "e4m3", beta: float = 4.0,
+                               linear_beta: float | None = 25.0, want_gate_up: bool = False,
+                               out: torch.Tensor | None = None, gate_up_out: torch.Tensor | None = None):
+    """situ_glu_grouped_fwd on MXFP8 operands.
+
+    x_codes [M, K] and weight_codes [E, 2I, K] hold fp8 codes (uint8, or the
+    torch float8 dtype of fp8_format), x_scales [M, K / 32] and weight_scales
+    [E, 2I, K / 32] their E8M0 scale bytes (uint8): element k of a row is
+    decode(code) * 2^(scale[k / 32] - 127).  The rest is as for
+    situ_glu_grouped_fwd."""
+    lib = _capi.load()
+    fmt = _mx_args(fp8_format, "floor")[0]
+    _check_device(x_codes, x_scales, weight_codes, weight_scales, group_offsets, routing_weights, out, gate_up_out)
+    ok = _FP8_CODE_DTYPES[fp8_format]
+    if x_codes.dtype not in ok or weight_codes.dtype not in ok:
+        raise TypeError(f"x_codes and weight_codes must be uint8 or {ok[1]} tensors")
+    if x_scales.dtype != torch.uint8 or weight_scales.dtype != torch.uint8:
+        raise TypeError("x_scales and weight_scales must be uint8 tensors")
+    ts = (x_codes, x_scales, weight_codes, weight_scales)
+    if x_codes.dim() != 2 or weight_codes.dim() != 3 or not all(t.is_contiguous() for t in ts):
+        raise ValueError("x_codes must be a contiguous [M, K] and weight_codes a contiguous [E, 2I, K] tensor")
+    rows, hidden = x_codes.shape
+    experts, two_i, k2 = weight_codes.shape
+    if k2 != hidden or two_i % 2:
+        raise ValueError(f"weight_codes must be [E, 2I, {hidden}], got {tuple(weight_codes.shape)}")
+    if hidden % _capi.SITU_MX_BLOCK:
+        raise ValueError(f"hidden must be a multiple of {_capi.SITU_MX_BLOCK}, got {hidden}")
+    sb = hidden // _capi.SITU_MX_BLOCK
+    if tuple(x_scales.shape) != (rows, sb) or tuple(weight_scales.shape) != (experts, two_i, sb):
+        raise ValueError(f"x_scales must be [{rows}, {sb}] and weight_scales [{experts}, {two_i}, {sb}]")
+    rwd, rw_rows, out, gate_up_out = _grouped_outputs(rows, experts, two_i, group_offsets, routing_weights, out,
+                                                      want_gate_up, gate_up_out, x_codes.device)
+    _capi.check(lib.situ_glu_grouped_fwd_mxfp8(
+        x_codes.data_ptr(), x_scales.data_ptr(), rows, hidden, weight_codes.data_ptr(), weight_scales.data_ptr(),
+        experts, two_i // 2, fmt, group_offsets.data_ptr(), routing_weights.data_ptr(), rwd, rw_rows, float(beta),
+        _capi.lb_ptr(linear_beta), out.data_ptr(), gate_up_out.data_ptr() if gate_up_out is not None else None,
+        _stream()), lib)
     return (out, gate_up_out) if gate_up_out is not None else out
 
 

@@ -57,6 +57,18 @@ group sizes -> x -> weight -> routing weights):
                 bf16; weight ~ N(0, 1/sqrt(7168)) bf16 (projections of unit
                 scale); routing weights = softmax over 8 N(0, 1) draws per token
                 (the routed_top8 recipe), fp32; beta 4, linear_beta 25.
+  grouped_fc1_top8_mxfp8
+                the grouped_fc1_top8 shape on MXFP8 operands
+                (make_grouped_mx_inputs; draws in the order group sizes ->
+                x codes -> x scales -> weight codes -> weight scales ->
+                routing weights): codes = the E4M3 (or E5M2) bytes of
+                64 N(0, 1) clamped to the format's largest finite value
+                (a block quantiser maps a block's largest value near the top
+                of the element range), x scale bytes uniform in 118 .. 122,
+                weight scale bytes uniform in 113 .. 117 (per 32 values along
+                hidden; the decoded x is then of order 2^-3 .. 2, the decoded
+                weight of order 2^-8 .. 2^-4, projections of order 1); routing
+                weights and group sizes as above.
 """
 from __future__ import annotations
 
@@ -284,4 +296,67 @@ def make_grouped_inputs(rows: int, experts: int, hidden: int, inter: int, device
 def grouped_flops(name: str) -> int:
     """Floating-point operations of the projections: 2 M K (2 I)."""
     w = GROUPED[name]
+    return 2 * w.rows * w.hidden * 2 * w.inter
+
+
+GROUPED_MX = {
+    "grouped_fc1_top8_mxfp8": GroupedWorkload("grouped_fc1_top8_mxfp8", 65536, 16, 7168, 2048, 4.0, 25.0,
+                                              "fused FC1 grouped GEMM + SiTU-GLU on MXFP8 (E4M3) x and weight, "
+                                              "65536 routed rows over 16 experts, hidden 7168, intermediate "
+                                              "2048, bf16 output"),
+}
+
+_FP8_TORCH = {"e4m3": (torch.float8_e4m3fn, 448.0), "e5m2": (torch.float8_e5m2, 57344.0)}
+
+
+def make_grouped_mx_inputs(rows: int, experts: int, hidden: int, inter: int, fp8_format: str = "e4m3",
+                           device="cpu", seed: int = 0, counts=None, rw_mode: str = "top8") -> dict:
+    """Seeded MXFP8 operands for the fused grouped GEMM (recipe in the module
+    doc): uint8 codes and E8M0 scale bytes of x [rows, hidden] and weight
+    [experts, 2 inter, hidden], group offsets and routing weights."""
+    if hidden % 32:
+        raise ValueError("hidden must be a multiple of 32")
+    dt, fmax = _FP8_TORCH[fp8_format]
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    if counts is None:
+        p = torch.softmax(0.5 * torch.randn(experts, generator=gen, device=dev), 0)
+        idx = torch.multinomial(p, rows, replacement=True, generator=gen) if rows else \
+            torch.zeros(0, dtype=torch.int64, device=dev)
+        counts = torch.bincount(idx, minlength=experts).cpu().tolist()
+    counts = [int(c) for c in counts]
+    if len(counts) != experts or sum(counts) != rows:
+        raise ValueError("counts must hold one count per expert summing to rows")
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + c)
+
+    def codes(*shape):
+        v = (64.0 * torch.randn(*shape, generator=gen, device=dev)).clamp(-fmax, fmax)
+        return v.to(dt).view(torch.uint8).contiguous()
+
+    sb = hidden // 32
+    xc = codes(rows, hidden)
+    xs = torch.randint(118, 123, (rows, sb), generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
+    wc = codes(experts, 2 * inter, hidden)
+    ws = torch.randint(113, 118, (experts, 2 * inter, sb), generator=gen, device=dev,
+                       dtype=torch.int32).to(torch.uint8)
+    if rw_mode == "top8":
+        if rows % 8:
+            raise ValueError("top8 routing weights need rows to be a multiple of 8")
+        rw = torch.softmax(torch.randn(rows // 8, 8, generator=gen, device=dev), 1).reshape(rows).contiguous()
+    elif rw_mode == "uniform":
+        rw = torch.rand(rows, generator=gen, device=dev)
+    elif rw_mode == "one":
+        rw = torch.ones(1, device=dev)
+    else:
+        raise ValueError(rw_mode)
+    return {"x_codes": xc, "x_scales": xs, "weight_codes": wc, "weight_scales": ws, "fp8_format": fp8_format,
+            "offsets": offsets, "counts": counts, "routing_weights": rw}
+
+
+def grouped_mx_flops(name: str) -> int:
+    """Floating-point operations of the projections: 2 M K (2 I)."""
+    w = GROUPED_MX[name]
     return 2 * w.rows * w.hidden * 2 * w.inter

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 4
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 5
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -234,6 +234,66 @@ def test_grouped_python_layer_rejects():
     with pytest.raises((TypeError, ValueError)):
         situ_glu_grouped_fwd(torch.zeros(4, 64), torch.zeros(2, 256, 64), torch.zeros(3, dtype=torch.int32),
                              torch.ones(4))
+
+
+def _grouped_mx(lib, **kw):
+    lb = ctypes.c_double(25.0)
+    a = dict(x=FAKE, xs=FAKE + 1024, rows=4, hidden=128, w=FAKE + 4096, ws=FAKE + 69632, experts=2, inter=128,
+             fmt=0, off=FAKE + 71680, rw=FAKE + 71696, rwd=0, rw_rows=4, beta=4.0, lb=ctypes.byref(lb),
+             out=FAKE + 73728, gu=FAKE + 81920)
+    a.update(kw)
+    return lib.situ_glu_grouped_fwd_mxfp8(a["x"], a["xs"], a["rows"], a["hidden"], a["w"], a["ws"], a["experts"],
+                                          a["inter"], a["fmt"], a["off"], a["rw"], a["rwd"], a["rw_rows"],
+                                          a["beta"], a["lb"], a["out"], a["gu"], None)
+
+
+# x codes 4 x 128 bytes at FAKE; x scales 16 bytes at FAKE + 1024; weight codes
+# 2 x 256 x 128 = 65536 bytes at FAKE + 4096; weight scales 2048 bytes at
+# FAKE + 69632; offsets 12 bytes at FAKE + 71680; routing weights 16 bytes at
+# FAKE + 71696; out 1024 bytes at FAKE + 73728; gate_up 2048 bytes at FAKE + 81920
+BAD_GROUPED_MX = [
+    dict(fmt=2), dict(fmt=-1), dict(rwd=3), dict(beta=0.0), dict(rows=-1), dict(experts=0), dict(rw_rows=3),
+    dict(x=None), dict(xs=None), dict(w=None), dict(ws=None), dict(off=None), dict(out=None),
+    dict(x=FAKE + 8), dict(w=FAKE + 4104), dict(xs=FAKE + 1026), dict(ws=FAKE + 69634), dict(out=FAKE + 73736),
+    dict(out=FAKE + 70656),                            # overlaps the weight scales
+    dict(gu=FAKE + 1024),                              # overlaps the x scales
+    dict(out=FAKE + 81920 - 512),                      # overlaps gate_up_out
+    dict(experts=4097),
+]
+
+
+@pytest.mark.parametrize("kw", BAD_GROUPED_MX, ids=[str(k) for k in BAD_GROUPED_MX])
+def test_grouped_mx_rejects(lib, capi, kw):
+    assert _grouped_mx(lib, **kw) == capi.SITU_ERR_INVALID_ARG, kw
+    assert capi.last_error(lib) != ""
+
+
+def test_grouped_mx_empty_and_unsupported(lib, capi):
+    assert _grouped_mx(lib, rows=0, rw_rows=0, x=None, xs=None, out=None, gu=None) == capi.SITU_OK
+    assert _grouped_mx(lib, inter=0, out=None, gu=None) == capi.SITU_OK
+    assert _grouped_mx(lib, hidden=64) == capi.SITU_ERR_UNSUPPORTED      # not a multiple of 128
+    assert _grouped_mx(lib, hidden=192) == capi.SITU_ERR_UNSUPPORTED
+    assert _grouped_mx(lib, inter=192) == capi.SITU_ERR_UNSUPPORTED
+    assert _grouped_mx(lib, rows=(1 << 31) - 1, rw_rows=1, inter=1 << 20) == capi.SITU_ERR_UNSUPPORTED
+
+
+def test_grouped_mx_python_layer_rejects():
+    import torch
+
+    from ffn_gated_activation_amd import situ_glu_grouped_fwd_mxfp8
+    u8 = torch.uint8
+    good = dict(x_codes=torch.zeros(4, 128, dtype=u8), x_scales=torch.zeros(4, 4, dtype=u8),
+                weight_codes=torch.zeros(2, 256, 128, dtype=u8), weight_scales=torch.zeros(2, 256, 4, dtype=u8),
+                group_offsets=torch.zeros(3, dtype=torch.int32), routing_weights=torch.ones(4))
+    for bad in (dict(x_codes=torch.zeros(4, 128)),                      # float codes
+                dict(x_scales=torch.zeros(4, 4, dtype=torch.int32)),    # wrong scale dtype
+                dict(x_scales=torch.zeros(4, 3, dtype=u8)),             # wrong scale shape
+                dict(weight_codes=torch.zeros(2, 256, 96, dtype=u8)),   # hidden mismatch
+                dict(fp8_format="e3m4")):
+        with pytest.raises((TypeError, ValueError)):
+            situ_glu_grouped_fwd_mxfp8(**{**good, **bad})
+    with pytest.raises((TypeError, ValueError)):  # e5m2 float8 codes under the e4m3 format
+        situ_glu_grouped_fwd_mxfp8(**{**good, "x_codes": torch.zeros(4, 128, dtype=torch.float8_e5m2)})
 
 
 def test_attn_res_empty_and_unsupported(lib, capi):
