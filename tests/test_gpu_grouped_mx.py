@@ -144,3 +144,27 @@ def test_grouped_mx_full_workload_sampled():
     ratio_gu = assert_gate_up_close("full", gu[idx], ref, wl.hidden, mx_exp=mx_exp)
     print(f"[grouped_mx] full: {len(rows)} sampled rows, max error / bound {ratio:.3g} (projections "
           f"{ratio_gu:.3g})", flush=True)
+
+
+def test_grouped_mx_partial_scale_group_does_not_leak():
+    """hidden 640: 5 stages of 128, so the last 16-byte scale group of a row
+    runs into the next row's first scale bytes.  A NaN scale (byte 255) at
+    the start of x row 51 and of weight row 11 must reach only that row's /
+    that column's results."""
+    hidden, inter = 640, 128
+    inp = make_grouped_mx_inputs(300, 2, hidden, inter, "e4m3", seed=17, counts=[150, 150], rw_mode="uniform")
+    inp["x_scales"][51, 0] = 255
+    inp["weight_scales"][0, 11, 0] = 255
+    out = _run(inp, 4.0, 25.0)
+    torch.cuda.synchronize()
+    ref, mx_exp = _oracle(inp, 4.0, 25.0)
+    from grouped_compare import output_bound
+    bound = output_bound(ref, hidden, 4.0, 25.0, mx_exp)
+    y = out.double().cpu().numpy()
+    keep = np.ones_like(y, dtype=bool)
+    keep[51, :] = False
+    keep[:150, 11] = False        # expert 0's gate column 11
+    assert np.isfinite(ref["out"][keep]).all()
+    err = np.abs(y - ref["out"])
+    bad = keep & ~(err <= bound)
+    assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, first at {np.argwhere(bad)[0]}"
