@@ -7,9 +7,10 @@ One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
 inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
 forward with MXFP8 output instead (forward only); attn_res_mix times the
-attention-residual mixing kernel; grouped_fc1_top8 times the fused FC1
-grouped GEMM + SiTU-GLU (value and roofline in TFLOP/s against the bf16
-matrix-core peak).  W untimed steps, then K timed steps between two device
+attention-residual mixing kernel; grouped_fc1_top8 (bf16 operands) and
+grouped_fc1_top8_mxfp8 (MXFP8 operands) time the fused FC1 grouped GEMM +
+SiTU-GLU (value and roofline in TFLOP/s against the matrix-core peak of the
+operand type).  W untimed steps, then K timed steps between two device
 synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
@@ -21,6 +22,12 @@ synchronisations.  Prints ONE JSON line:
                back-to-back launches of that kernel
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
                (a reported baseline, not the target)
+  cold_cache_and_ceilings
+               (elementwise workloads) the median of each kernel's launches
+               with a 512 MiB read before each one (nothing left in L2 or the
+               Infinity Cache), and a plain copy and bf16 add of the same
+               sizes, warm and cold, as measured ceilings of their read:write
+               mixes
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -30,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -188,6 +196,51 @@ def bench_attn_res(args) -> int:
     return 0
 
 
+def _median_ms(fn, n, flush=None) -> float:
+    """Median duration of n launches of fn, each between two HIP events on
+    the launch stream; with `flush`, a read of 512 MiB (not timed) runs
+    before every launch so that nothing the launch reads is left in L2 or the
+    Infinity Cache.  A read, not a fill: a fill leaves up to the Infinity
+    Cache's 256 MB of dirty lines, whose write-back the timed launch would
+    then pay for."""
+    import torch
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush.amax()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return statistics.median(ts)
+
+
+def _cold_and_ceilings(kernels: dict, nbytes: dict, rows: int, inter: int, n: int, dev) -> dict:
+    """Cold-cache medians of the path's kernels, and plain elementwise kernels
+    of the same byte counts for scale: a copy (1 read : 1 write) and a bf16
+    add (2 : 1, the forward's mix), timed warm (back to back) and cold."""
+    import torch
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    out = {"flush_bytes_read": 512 << 20, "launches": n}
+    for name, fn in kernels.items():
+        ms = _median_ms(fn, n, flush)
+        out[f"{name}_cold"] = {"ms": round(ms, 5), "GB/s": round(nbytes[name] / (ms / 1e3) / 1e9, 2)}
+    a = torch.empty(rows, inter, dtype=torch.bfloat16, device=dev).normal_()
+    b = torch.empty_like(a).normal_()
+    c = torch.empty_like(a)
+    e = a.numel() * 2
+    for name, fn, nb in (("copy_1to1", lambda: c.copy_(a), 2 * e), ("add_2to1", lambda: torch.add(a, b, out=c), 3 * e)):
+        warm = _median_ms(fn, n)
+        cold = _median_ms(fn, n, flush)
+        out[name] = {"bytes": nb, "warm_GB/s": round(nb / (warm / 1e3) / 1e9, 2),
+                     "cold_GB/s": round(nb / (cold / 1e3) / 1e9, 2)}
+    del flush
+    return out
+
+
 def _cpu_baseline_grouped(name: str, sample_rows: int) -> dict:
     import oracle
     from threadpoolctl import threadpool_limits
@@ -337,6 +390,8 @@ def main(argv=None) -> int:
                     help="rows of the CPU-oracle sample of the grouped GEMM workload")
     ap.add_argument("--compare-unfused", action="store_true",
                     help="grouped GEMM workload: also time torch._grouped_mm + the activation kernel (context)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache medians and the plain-kernel ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration runs)")
     args = ap.parse_args(argv)
@@ -419,6 +474,10 @@ def main(argv=None) -> int:
     _copy_calibration(args, dev)
 
     ab = algorithmic_bytes(args.workload)
+    cold = None
+    if not args.no_cold:
+        ks = {"fwd": fwd, "bwd": bwd} if w.backward else {"fwd": fwd}
+        cold = _cold_and_ceilings(ks, ab, w.rows, w.inter, min(args.steps, 20), dev)
     ms_per_step = wall / args.steps * 1e3
     value = ab["total"] / (ms_per_step / 1e3) / 1e9
     dom = "bwd" if w.backward else "fwd"
@@ -457,6 +516,7 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(args.workload, dom, src)},
+        "cold_cache_and_ceilings": cold,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
