@@ -153,9 +153,10 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     // not make those reads wait for the loads in flight.
     __shared__ __attribute__((aligned(1024))) char smem0[kBufBytes];
     __shared__ __attribute__((aligned(1024))) char smem1[kBufBytes];
-    // fp8: scale bytes of four stages (16 blocks of 32: 16 bytes) per x row
-    // (0..255) and per gate / up row (256..511); two such groups, used in turn
-    __shared__ __attribute__((aligned(16))) uint4 sscg[F8 ? 2 : 1][F8 ? 2 * kBM : 1];
+    // fp8: the stage's scale bytes, one dword (4 blocks of 32) per x row (0..255)
+    // and per gate / up row (256..511), per buffer
+    __shared__ __attribute__((aligned(16))) uint32_t ssc0[F8 ? 2 * kBM : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t ssc1[F8 ? 2 * kBM : 1];
     __shared__ float s_rs[kBM];
     __shared__ int s_expert;
 
@@ -219,8 +220,7 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     }
     const int nk = hidden / kStageK;
     const rsrc_t rz = make_rsrc(xb, 0u);  // reads as zero: the padding stage of an odd count
-    // fp8 scales: row r's bytes for stage kt are the dword at r * (K / 32) + 4 kt;
-    // stages 4 g .. 4 g + 3 form scale group g (16 bytes per row)
+    // fp8 scales: row r's bytes for stage kt are the dword at r * (K / 32) + 4 kt
     const uint32_t sbytes = (uint32_t)hidden / 32u;
     rsrc_t rsa = rz, rsg = rz, rsu = rz;
     if (F8) {
@@ -229,20 +229,17 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
         rsg = make_rsrc(wsb, (uint32_t)kBN * sbytes);
         rsu = make_rsrc(wsb + ((int64_t)inter - kBN) * sbytes, (uint32_t)(2 * kBN) * sbytes);
     }
-    // wavefront wv loads scale group g of x rows and of w rows 64 wv..64 wv + 63
-    // (one 16-byte load each); the bytes of a row's last, partial group run
-    // into the next row and belong to stages past the last, whose scales are
-    // read from elsewhere (read_scales)
-    auto issue_scale_group = [&](int g) {
-        if constexpr (F8) {
-            uint4 *base = sscg[g & 1];
-            const bool live = 16u * (uint32_t)g < sbytes;
-            const uint32_t vo = (uint32_t)(64 * wv + lane) * sbytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rz, (lds_ptr_t)(base + 64 * wv), 16, (int)vo,
-                                                     16 * g, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? (wv < 2 ? rsg : rsu) : rz,
-                                                     (lds_ptr_t)(base + kBM + 64 * wv), 16, (int)vo, 16 * g, 0, 0);
-        }
+    // wavefront wv loads the scale dwords of x rows and of w rows 64 wv..64 wv + 63
+    auto issue_scales = [&](int kt, auto buf) {
+        if (!F8)
+            return;
+        uint32_t *base = decltype(buf)::value ? ssc1 : ssc0;
+        const bool live = kt < nk;
+        const uint32_t vo = (uint32_t)(64 * wv + lane) * sbytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rz, (lds_ptr_t)(base + 64 * wv), 4, (int)vo,
+                                                 kt * 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? (wv < 2 ? rsg : rsu) : rz,
+                                                 (lds_ptr_t)(base + kBM + 64 * wv), 4, (int)vo, kt * 4, 0, 0);
     };
     auto issue = [&](int kt, auto buf, int j0 = 0, int j1 = kLoads) {
         const uint32_t so = (uint32_t)kt * kRowB;
@@ -317,20 +314,14 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     struct Scales {
         uint32_t a[4], g[2], u[2];
     };
-    auto read_scales = [&](int kt, Scales &q) {
-        // dword kt % 4 of each row's entry in group kt / 4 (row stride 4
-        // dwords).  A stage past the last one reads its own stage buffer
-        // instead, which its empty-descriptor loads filled with zeros (a
-        // choice of base address, not a select per value)
-        const uint32_t *sc = kt < nk ? reinterpret_cast<const uint32_t *>(sscg[(kt >> 2) & 1]) + (kt & 3)
-                                     : reinterpret_cast<const uint32_t *>((kt & 1) ? smem1 : smem0);
+    auto read_scales = [&](const uint32_t *sc, Scales &q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            q.a[i] = sc[4 * (wm * 128 + i * 32 + l32)];
+            q.a[i] = sc[wm * 128 + i * 32 + l32];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            q.g[j] = sc[4 * (kBM + wn * 64 + j * 32 + l32)];
-            q.u[j] = sc[4 * (kBM + kBN + wn * 64 + j * 32 + l32)];
+            q.g[j] = sc[kBM + wn * 64 + j * 32 + l32];
+            q.u[j] = sc[kBM + kBN + wn * 64 + j * 32 + l32];
         }
     };
     constexpr int kCbsz = OP == OP_E5M2 ? 1 : 0;  // operand format of the scaled product (same for both)
@@ -399,64 +390,45 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     // landed, one barrier; then the next stage's first fragments (and
     // scales) and the loads of stage kt_next (into `buf`) go out while the
     // last 16 products of the stage run
-    auto boundary = [&](auto buf, int kt_next, auto group) {
+    auto boundary = [&](auto buf, int kt_next) {
         constexpr int nb = 1 - decltype(buf)::value;
         const Scales &q = decltype(buf)::value ? q1 : q0;
         wait_vmcnt<0>();
         __syncthreads();
         read_frags(nb ? smem1 : smem0, 0, f0);
         if (F8)
-            read_scales(kt_next - 1, nb ? q1 : q0);
+            read_scales(nb ? ssc1 : ssc0, nb ? q1 : q0);
+        issue_scales(kt_next, buf);
         issue(kt_next, buf, 0, kFirst);
         mfmas(f1, q, kSteps - 1);
         __builtin_amdgcn_sched_group_barrier(0x100, F8 ? kFragReads + 8 : kFragReads, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i % kSpread == 0 && i / kSpread < kFirst)
+            if (i % kSpread == 0 && i / kSpread < kFirst + (F8 ? 2 : 0))
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // fp8: entering the first stage of scale group g, the loads of group
-        // g + 1 go out (every wavefront has read group g - 1, the other
-        // buffer, before the barrier above)
-        if constexpr (decltype(group)::value)
-            issue_scale_group(((kt_next - 1) >> 2) + 1);
     };
 
     // ---- main loop.  Stage kt lives in buffer kt % 2; the loads of stage
     // kt + 1 are in flight while stage kt is multiplied.  The body is two
-    // stages (one per buffer; fp8: four, one scale group) with no tail: the
-    // stage count is padded with stages of zeros (an empty descriptor),
-    // which add nothing.
-    issue_scale_group(0);
+    // stages (one per buffer) with no tail: an odd stage count gets one more
+    // stage of zeros (an empty descriptor), which adds nothing.
+    issue_scales(0, Buf0{});
     issue(0, Buf0{});
     wait_vmcnt<0>();
     __syncthreads();
     read_frags(smem0, 0, f0);
     if (F8)
-        read_scales(0, q0);
-    issue_scale_group(1);
+        read_scales(ssc0, q0);
+    issue_scales(1, Buf1{});
     issue(1, Buf1{}, 0, kFirst);
-    using NoGroup = std::false_type;
-    if constexpr (F8) {
-        for (int kt = 0; kt < nk; kt += 4) {
-            first_steps(Buf0{}, kt + 1);
-            boundary(Buf0{}, kt + 2, NoGroup{});
-            first_steps(Buf1{}, kt + 2);
-            boundary(Buf1{}, kt + 3, NoGroup{});
-            first_steps(Buf0{}, kt + 3);
-            boundary(Buf0{}, kt + 4, NoGroup{});
-            first_steps(Buf1{}, kt + 4);
-            boundary(Buf1{}, kt + 5, std::true_type{});  // entering stage kt + 4, group kt / 4 + 1
-        }
-    } else {
-        for (int kt = 0; kt < nk; kt += 2) {
-            first_steps(Buf0{}, kt + 1);
-            boundary(Buf0{}, kt + 2, NoGroup{});
-            first_steps(Buf1{}, kt + 2);
-            boundary(Buf1{}, kt + 3, NoGroup{});
-        }
+    for (int kt = 0; kt < nk; kt += 2) {
+        first_steps(Buf0{}, kt + 1);
+        boundary(Buf0{}, kt + 2);
+        first_steps(Buf1{}, kt + 2);
+        boundary(Buf1{}, kt + 3);
     }
     wait_vmcnt<0>();  // loads past the last stage (zeros) have landed
     __syncthreads();  // every wavefront is done with the stage buffers

@@ -96,6 +96,14 @@ def test_grouped_uncovered_rows_untouched():
     assert_grouped_close("uncovered", out, ref, 128, 4.0, 25.0, rows=torch.from_numpy(rows))
 
 
+def test_grouped_max_experts():
+    """SITU_GROUPED_MAX_EXPERTS experts, most with 0 to 2 rows: every
+    workgroup scans all 4097 offsets to find its expert."""
+    from ffn_gated_activation_amd._capi import SITU_GROUPED_MAX_EXPERTS
+    inp = make_grouped_inputs(3000, SITU_GROUPED_MAX_EXPERTS, 64, 128, seed=23, rw_mode="uniform")
+    _check_all("max_experts", inp, 4.0, 25.0, False)
+
+
 def test_grouped_empty():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
     w = torch.zeros(2, 256, 64, dtype=torch.bfloat16, device=DEV)

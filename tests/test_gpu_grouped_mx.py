@@ -113,6 +113,15 @@ def test_grouped_mx_uncovered_rows_untouched():
     assert_grouped_close("uncovered", out, ref, 128, 4.0, 25.0, rows=torch.from_numpy(rows), mx_exp=mx_exp)
 
 
+def test_grouped_mx_max_experts():
+    from ffn_gated_activation_amd._capi import SITU_GROUPED_MAX_EXPERTS
+    inp = make_grouped_mx_inputs(3000, SITU_GROUPED_MAX_EXPERTS, 128, 128, "e5m2", seed=29, rw_mode="uniform")
+    out = _run(inp, 4.0, 25.0)
+    torch.cuda.synchronize()
+    ref, mx_exp = _oracle(inp, 4.0, 25.0)
+    assert_grouped_close("max_experts", out, ref, 128, 4.0, 25.0, mx_exp=mx_exp)
+
+
 def test_grouped_mx_empty():
     u8 = torch.uint8
     out = situ_glu_grouped_fwd_mxfp8(torch.empty(0, 128, dtype=u8, device=DEV), torch.empty(0, 4, dtype=u8,
