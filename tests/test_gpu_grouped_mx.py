@@ -155,11 +155,11 @@ def test_grouped_mx_full_workload_sampled():
           f"{ratio_gu:.3g})", flush=True)
 
 
-def test_grouped_mx_partial_scale_group_does_not_leak():
-    """hidden 640: 5 stages of 128, so the last 16-byte scale group of a row
-    runs into the next row's first scale bytes.  A NaN scale (byte 255) at
-    the start of x row 51 and of weight row 11 must reach only that row's /
-    that column's results."""
+def test_grouped_mx_nan_scale_does_not_leak():
+    """hidden 640: 5 stages of 128 (an odd count: the loop adds a stage of
+    zeros, whose scales come from an empty descriptor).  A NaN scale (byte
+    255) at the start of x row 51 and of weight row 11, the bytes right after
+    rows 50 and 10, must reach only that row's / that column's results."""
     hidden, inter = 640, 128
     inp = make_grouped_mx_inputs(300, 2, hidden, inter, "e4m3", seed=17, counts=[150, 150], rw_mode="uniform")
     inp["x_scales"][51, 0] = 255
