@@ -28,13 +28,14 @@ SITU_MX_BLOCK = 32
 SITU_GROUPED_MAX_EXPERTS = 4096
 SITU_GROUPED_MAX_HIDDEN = 1 << 20
 SITU_GROUPED_MAX_INTERMEDIATE = 1 << 20
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # every symbol include/situ_glu.h declares
 EXPORTED = ("situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes",
             "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window",
             "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize", "situ_glu_attn_res_fwd",
-            "situ_glu_grouped_fwd", "situ_glu_grouped_fwd_mxfp8")
+            "situ_glu_grouped_fwd", "situ_glu_grouped_fwd_mxfp8",
+            "situ_glu_grouped_fwd_mxfp8_workspace_bytes")
 
 
 class SituGluError(RuntimeError):
@@ -73,7 +74,9 @@ def _bind(lib):
                                          vp]
     lib.situ_glu_grouped_fwd_mxfp8.restype = i32
     lib.situ_glu_grouped_fwd_mxfp8.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64, i32, vp, vp, i32, i64, dbl,
-                                                dblp, vp, vp, vp]
+                                                dblp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.situ_glu_grouped_fwd_mxfp8_workspace_bytes.restype = ctypes.c_size_t
+    lib.situ_glu_grouped_fwd_mxfp8_workspace_bytes.argtypes = [i64, i64, i64, i64]
     return lib
 
 

@@ -630,7 +630,7 @@ namespace {
 int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64_t hidden, const void *weight,
                 const void *w_scales, int64_t experts, int64_t intermediate, const int32_t *group_offsets,
                 const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta, const double *linear_beta,
-                void *out, void *gate_up_out, void *stream)
+                void *out, void *gate_up_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     const int64_t kstep = op ? 128 : 64;     // hidden elements of one pipeline stage
     const int64_t es = op ? 1 : 2;           // bytes per operand element
@@ -657,8 +657,20 @@ int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64
                     "workgroups", (long long)rows, (long long)experts, (long long)intermediate);
     if (!weight || !group_offsets || !out)
         return fail(SITU_ERR_INVALID_ARG, "weight, group_offsets or out is NULL");
+    const int64_t nk = hidden / 128, wrows = experts * 2 * intermediate;
+    if (op && (rows * nk >= ((int64_t)1 << 30) || wrows * nk >= ((int64_t)1 << 30)))
+        return fail(SITU_ERR_UNSUPPORTED, "rows * hidden / 128 and experts * 2 * intermediate * hidden / 128 must "
+                    "be below 2^30 on MXFP8 operands (got %lld and %lld)", (long long)(rows * nk),
+                    (long long)(wrows * nk));
     if (op && (!x_scales || !w_scales))
         return fail(SITU_ERR_INVALID_ARG, "x_scales or w_scales is NULL");
+    const int64_t need = op ? situ::grouped_mx_scale_bytes(rows, hidden) + situ::grouped_mx_scale_bytes(wrows, hidden)
+                            : 0;
+    if (op && (!workspace || workspace_bytes < (size_t)need))
+        return fail(SITU_ERR_INVALID_ARG, "workspace of %zu bytes at %p, %lld bytes needed", workspace_bytes,
+                    workspace, (long long)need);
+    if (op && !aligned16(workspace))
+        return fail(SITU_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     if (!aligned16(x) || !aligned16(weight) || !aligned16(out) || (gate_up_out && !aligned16(gate_up_out)))
         return fail(SITU_ERR_INVALID_ARG, "x, weight, out and gate_up_out must be 16-byte aligned");
     if (op && (!aligned_to(x_scales, 4) || !aligned_to(w_scales, 4)))
@@ -667,7 +679,8 @@ int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64
         return fail(SITU_ERR_INVALID_ARG, "group_offsets is not 4-byte aligned");
     const int64_t sb = hidden / 32;
     const Range outs[] = {range("out", out, rows * intermediate * 2),
-                          range("gate_up_out", gate_up_out, gate_up_out ? rows * intermediate * 4 : 0)};
+                          range("gate_up_out", gate_up_out, gate_up_out ? rows * intermediate * 4 : 0),
+                          range("workspace", workspace, need)};
     const Range ins[] = {range("x", x, rows * hidden * es),
                          range("weight", weight, experts * 2 * intermediate * hidden * es),
                          range("x_scales", x_scales, op ? rows * sb : 0),
@@ -678,8 +691,10 @@ int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64
         for (const Range &i : ins)
             if (overlaps(o, i))
                 return fail(SITU_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
-    if (overlaps(outs[0], outs[1]))
-        return fail(SITU_ERR_INVALID_ARG, "out overlaps gate_up_out");
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], outs[b]))
+                return fail(SITU_ERR_INVALID_ARG, "%s overlaps %s", outs[a].name, outs[b].name);
 
     situ::GroupedLaunch L{};
     L.op = op;
@@ -701,6 +716,7 @@ int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64
     L.fast = beta == 4.0;
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    L.workspace = op ? workspace : nullptr;
     const int err = situ::launch_grouped_fwd(L, stream);
     if (err)
         return fail(SITU_ERR_DEVICE, "grouped GEMM launch failed: %s", situ::device_error_string(err));
@@ -720,14 +736,25 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows, int64_t hidd
     if (io_dtype != SITU_DTYPE_BF16)
         return fail(SITU_ERR_UNSUPPORTED, "the grouped GEMM takes bf16 x and weight only (io_dtype %d)", io_dtype);
     return grouped_fwd(0, x, nullptr, rows, hidden, weight, nullptr, experts, intermediate, group_offsets,
-                       routing_weights, rw_dtype, rw_rows, beta, linear_beta, out, gate_up_out, stream);
+                       routing_weights, rw_dtype, rw_rows, beta, linear_beta, out, gate_up_out, nullptr, 0, stream);
+}
+
+size_t situ_glu_grouped_fwd_mxfp8_workspace_bytes(int64_t rows, int64_t hidden, int64_t experts,
+                                                  int64_t intermediate)
+{
+    if (rows < 0 || hidden < 0 || experts < 0 || intermediate < 0 || hidden > SITU_GROUPED_MAX_HIDDEN ||
+        experts > SITU_GROUPED_MAX_EXPERTS || intermediate > SITU_GROUPED_MAX_INTERMEDIATE ||
+        rows > (int64_t)0x7fffffff)
+        return 0;
+    return (size_t)(situ::grouped_mx_scale_bytes(rows, hidden) +
+                    situ::grouped_mx_scale_bytes(experts * 2 * intermediate, hidden));
 }
 
 int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales, int64_t rows, int64_t hidden,
                                const void *w_codes, const void *w_scales, int64_t experts, int64_t intermediate,
                                int fp8_format, const int32_t *group_offsets, const void *routing_weights,
                                int rw_dtype, int64_t rw_rows, double beta, const double *linear_beta, void *out,
-                               void *gate_up_out, void *stream)
+                               void *gate_up_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     g_last_error.clear();
     if (fp8_format != SITU_FP8_E4M3 && fp8_format != SITU_FP8_E5M2)
@@ -735,7 +762,7 @@ int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales, int64_
                     fp8_format);
     return grouped_fwd(fp8_format == SITU_FP8_E4M3 ? 1 : 2, x_codes, x_scales, rows, hidden, w_codes, w_scales,
                        experts, intermediate, group_offsets, routing_weights, rw_dtype, rw_rows, beta, linear_beta,
-                       out, gate_up_out, stream);
+                       out, gate_up_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

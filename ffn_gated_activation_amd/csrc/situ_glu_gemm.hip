@@ -35,6 +35,13 @@
 //   * the epilogue stages the bf16 results in LDS and writes whole 16-byte
 //     vectors of each row.
 //
+// MX fp8 operands: the kernel takes the E8M0 scale bytes stage-major, one
+// dword (the 4 scale bytes of a 128-wide stage) per row and stage, rows
+// contiguous: situ_mx_scales_stage_major_kernel rewrites the row-major MX
+// scale arrays that way first, so that one 64-lane load of a stage's scales
+// covers 64 consecutive rows (256 contiguous bytes) instead of touching 64
+// cache lines, one per row.
+//
 // Grouping on the device: the group offsets stay in device memory (a router
 // produces them there).  Row tiles are numbered by slots: expert e's tiles
 // occupy slots floor(offsets[e] / kBM) + e onwards, which never overlap the
@@ -220,26 +227,37 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     }
     const int nk = hidden / kStageK;
     const rsrc_t rz = make_rsrc(xb, 0u);  // reads as zero: the padding stage of an odd count
-    // fp8 scales: row r's bytes for stage kt are the dword at r * (K / 32) + 4 kt
-    const uint32_t sbytes = (uint32_t)hidden / 32u;
+    // fp8 scales, stage-major: the dword of row r for stage kt is at
+    // kt * R + r (R = rows for x, E * 2I for w; R * nk < 2^30, checked on the
+    // host, so byte offsets fit 32 bits).  The descriptors start at the
+    // tile's first row and end with the array: rows past the tile read other
+    // rows' scales, which only multiply the zero codes of those rows
+    // (results never stored)
+    const uint32_t sxs = (uint32_t)rows * 4u;
+    const uint32_t sws = (uint32_t)experts * 2u * (uint32_t)inter * 4u;
     rsrc_t rsa = rz, rsg = rz, rsu = rz;
     if (F8) {
-        rsa = make_rsrc(xs + (int64_t)row0 * sbytes, (uint32_t)nrows * sbytes);
-        const uint8_t *wsb = ws + ((int64_t)e * 2 * inter + n0) * sbytes;
-        rsg = make_rsrc(wsb, (uint32_t)kBN * sbytes);
-        rsu = make_rsrc(wsb + ((int64_t)inter - kBN) * sbytes, (uint32_t)(2 * kBN) * sbytes);
+        const uint32_t xend = (uint32_t)nk * sxs, wend = (uint32_t)nk * sws;
+        rsa = make_rsrc(xs + (int64_t)row0 * 4, xend - (uint32_t)row0 * 4u);
+        const uint32_t wg = ((uint32_t)e * 2u * (uint32_t)inter + (uint32_t)n0) * 4u;
+        const uint32_t wu = wg + ((uint32_t)inter - kBN) * 4u;
+        rsg = make_rsrc(ws + wg, wend - wg);
+        rsu = make_rsrc(ws + wu, wend - wu);
     }
-    // wavefront wv loads the scale dwords of x rows and of w rows 64 wv..64 wv + 63
+    // wavefront wv loads the stage's scale dwords of x rows and of w rows
+    // 64 wv..64 wv + 63 (the up rows via a base kBN rows early, as for the
+    // operands)
     auto issue_scales = [&](int kt, auto buf) {
         if (!F8)
             return;
         uint32_t *base = decltype(buf)::value ? ssc1 : ssc0;
         const bool live = kt < nk;
-        const uint32_t vo = (uint32_t)(64 * wv + lane) * sbytes;
+        const uint32_t vo = (uint32_t)(64 * wv + lane) * 4u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rz, (lds_ptr_t)(base + 64 * wv), 4, (int)vo,
-                                                 kt * 4, 0, 0);
+                                                 (int)((uint32_t)kt * sxs), 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? (wv < 2 ? rsg : rsu) : rz,
-                                                 (lds_ptr_t)(base + kBM + 64 * wv), 4, (int)vo, kt * 4, 0, 0);
+                                                 (lds_ptr_t)(base + kBM + 64 * wv), 4, (int)vo,
+                                                 (int)((uint32_t)kt * sws), 0, 0);
     };
     auto issue = [&](int kt, auto buf, int j0 = 0, int j1 = kLoads) {
         const uint32_t so = (uint32_t)kt * kRowB;
@@ -499,6 +517,45 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     }
 }
 
+// Row-major MX scales (R rows of nk dwords: a row's 4 scale bytes per
+// 128-wide stage) to stage-major (nk rows of R dwords).  A workgroup moves a
+// 64 x 64 tile through LDS: reads of 64 consecutive dwords of one row, writes
+// of 64 consecutive rows of one stage.
+constexpr int kTrTile = 64;
+
+__global__ __launch_bounds__(256) void situ_mx_scales_stage_major_kernel(const uint32_t *__restrict__ in,
+                                                                         uint32_t *__restrict__ out, int64_t R,
+                                                                         int nk)
+{
+    __shared__ uint32_t tile[kTrTile][kTrTile + 1];
+    const int64_t r0 = (int64_t)blockIdx.x * kTrTile;
+    const int s0 = blockIdx.y * kTrTile;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < kTrTile * kTrTile / 256; ++k) {
+        const int idx = t + 256 * k, i = idx / kTrTile, j = idx % kTrTile;
+        if (r0 + i < R && s0 + j < nk)
+            tile[i][j] = in[(r0 + i) * nk + s0 + j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTrTile * kTrTile / 256; ++k) {
+        const int idx = t + 256 * k, j = idx / kTrTile, i = idx % kTrTile;
+        if (r0 + i < R && s0 + j < nk)
+            out[(int64_t)(s0 + j) * R + r0 + i] = tile[i][j];
+    }
+}
+
+int launch_stage_major(const void *in, void *out, int64_t R, int nk, hipStream_t st)
+{
+    if (R <= 0 || nk <= 0)
+        return 0;
+    const dim3 grid((unsigned)((R + kTrTile - 1) / kTrTile), (unsigned)((nk + kTrTile - 1) / kTrTile));
+    hipLaunchKernelGGL(situ_mx_scales_stage_major_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), R, nk);
+    return (int)hipGetLastError();
+}
+
 using GemmFn = void (*)(const void *, const void *, const uint8_t *, const uint8_t *, const int32_t *, int64_t, int,
                         int, int, int, const void *, int, int64_t, void *, void *, GateK, UpK);
 
@@ -519,6 +576,8 @@ GemmFn pick(bool lb, bool fast, bool gu)
 
 int64_t grouped_slots(int64_t rows, int64_t experts) { return rows / kBM + experts; }
 
+int64_t grouped_mx_scale_bytes(int64_t rows, int64_t hidden) { return (rows * (hidden / 128) * 4 + 255) / 256 * 256; }
+
 int64_t grouped_grid_blocks(int64_t rows, int64_t experts, int64_t inter)
 {
     const int64_t slots = grouped_slots(rows, experts), ntn = inter / kBN;
@@ -534,11 +593,26 @@ int launch_grouped_fwd(const GroupedLaunch &L, void *stream)
     if (blocks > 0x7fffffff)
         return (int)hipErrorInvalidConfiguration;  // the host API rejects such shapes first
     const bool gu = L.gate_up != nullptr;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const void *xs = L.x_scales, *ws = L.w_scales;
+    if (L.op != OP_BF16) {
+        // scales to stage-major in the workspace: x first, then the weights
+        char *wsp = static_cast<char *>(L.workspace);
+        const int nk = L.hidden / 128;
+        const int64_t wrows = (int64_t)L.experts * 2 * L.inter;
+        int err = launch_stage_major(L.x_scales, wsp, L.rows, nk, st);
+        if (!err)
+            err = launch_stage_major(L.w_scales, wsp + grouped_mx_scale_bytes(L.rows, L.hidden), wrows, nk, st);
+        if (err)
+            return err;
+        xs = wsp;
+        ws = wsp + grouped_mx_scale_bytes(L.rows, L.hidden);
+    }
     const GemmFn fn = L.op == OP_E4M3 ? pick<OP_E4M3>(L.lb, L.fast, gu)
                       : L.op == OP_E5M2 ? pick<OP_E5M2>(L.lb, L.fast, gu)
                                         : pick<OP_BF16>(L.lb, L.fast, gu);
-    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), L.x, L.w,
-                       static_cast<const uint8_t *>(L.x_scales), static_cast<const uint8_t *>(L.w_scales), L.offsets,
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, st, L.x, L.w,
+                       static_cast<const uint8_t *>(xs), static_cast<const uint8_t *>(ws), L.offsets,
                        L.rows, L.hidden, L.experts, L.inter, slots, L.rw, L.rw_bf16, L.rw_stride, L.out, L.gate_up,
                        L.gk, L.uk);
     return (int)hipGetLastError();

@@ -131,7 +131,10 @@ struct AresLaunch {
 // 2 inter, hidden], offsets [experts + 1] int32 in device memory; bf16
 // operands (hidden a multiple of 64) or MX fp8 codes with scale bytes
 // [rows, hidden / 32] and [experts, 2 inter, hidden / 32] (hidden a multiple
-// of 128); inter a multiple of 128; operands 16-byte aligned.
+// of 128; the launch first rewrites them stage-major into `workspace`,
+// grouped_mx_scale_bytes(rows, hidden) + grouped_mx_scale_bytes(experts *
+// 2 inter, hidden) bytes, 256-byte aligned); inter a multiple of 128;
+// operands 16-byte aligned.
 struct GroupedLaunch {
     int op;               // 0 bf16, 1 MX E4M3, 2 MX E5M2
     const void *x;
@@ -152,7 +155,10 @@ struct GroupedLaunch {
     int fast;
     GateK gk;
     UpK uk;
+    void *workspace;      // fp8: stage-major scales (see above)
 };
+// Bytes of one stage-major scale array of `rows` rows (256-byte multiple).
+int64_t grouped_mx_scale_bytes(int64_t rows, int64_t hidden);
 // Row-tile slots of the grouped GEMM grid (floor(rows / 256) + experts) and
 // the workgroups of its launch.
 int64_t grouped_slots(int64_t rows, int64_t experts);

@@ -316,14 +316,16 @@ def situ_glu_grouped_fwd_mxfp8(x_codes: torch.Tensor, x_scales: torch.Tensor, we
                                weight_scales: torch.Tensor, group_offsets: torch.Tensor,
                                routing_weights: torch.Tensor, fp8_format: str = "e4m3", beta: float = 4.0,
                                linear_beta: float | None = 25.0, want_gate_up: bool = False,
-                               out: torch.Tensor | None = None, gate_up_out: torch.Tensor | None = None):
+                               out: torch.Tensor | None = None, gate_up_out: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None):
     """situ_glu_grouped_fwd on MXFP8 operands.
 
     x_codes [M, K] and weight_codes [E, 2I, K] hold fp8 codes (uint8, or the
     torch float8 dtype of fp8_format), x_scales [M, K / 32] and weight_scales
     [E, 2I, K / 32] their E8M0 scale bytes (uint8): element k of a row is
-    decode(code) * 2^(scale[k / 32] - 127).  The rest is as for
-    situ_glu_grouped_fwd."""
+    decode(code) * 2^(scale[k / 32] - 127).  workspace: a device buffer of at
+    least situ_glu_grouped_fwd_mxfp8_workspace_bytes(...) bytes (allocated
+    here when not given).  The rest is as for situ_glu_grouped_fwd."""
     lib = _capi.load()
     fmt = _mx_args(fp8_format, "floor")[0]
     _check_device(x_codes, x_scales, weight_codes, weight_scales, group_offsets, routing_weights, out, gate_up_out)
@@ -346,12 +348,22 @@ def situ_glu_grouped_fwd_mxfp8(x_codes: torch.Tensor, x_scales: torch.Tensor, we
         raise ValueError(f"x_scales must be [{rows}, {sb}] and weight_scales [{experts}, {two_i}, {sb}]")
     rwd, rw_rows, out, gate_up_out = _grouped_outputs(rows, experts, two_i, group_offsets, routing_weights, out,
                                                       want_gate_up, gate_up_out, x_codes.device)
+    need = situ_glu_grouped_fwd_mxfp8_workspace_bytes(rows, hidden, experts, two_i // 2)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x_codes.device)
+    _check_device(workspace)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     _capi.check(lib.situ_glu_grouped_fwd_mxfp8(
         x_codes.data_ptr(), x_scales.data_ptr(), rows, hidden, weight_codes.data_ptr(), weight_scales.data_ptr(),
         experts, two_i // 2, fmt, group_offsets.data_ptr(), routing_weights.data_ptr(), rwd, rw_rows, float(beta),
         _capi.lb_ptr(linear_beta), out.data_ptr(), gate_up_out.data_ptr() if gate_up_out is not None else None,
-        _stream()), lib)
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()), lib)
     return (out, gate_up_out) if gate_up_out is not None else out
+
+
+def situ_glu_grouped_fwd_mxfp8_workspace_bytes(rows: int, hidden: int, experts: int, intermediate: int) -> int:
+    return int(_capi.load().situ_glu_grouped_fwd_mxfp8_workspace_bytes(rows, hidden, experts, intermediate))
 
 
 def situ_glu_last_error() -> str:

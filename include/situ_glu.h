@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 5
+#define SITU_GLU_ABI_VERSION 6
 
 /* return codes */
 #define SITU_OK 0
@@ -342,13 +342,23 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows,
  *   rw_rows, beta, linear_beta, out, gate_up_out, stream   as for
  *                  situ_glu_grouped_fwd
  *   fp8_format     SITU_FP8_E4M3 or SITU_FP8_E5M2 (x and weight alike)
- * x_codes, w_codes, out and gate_up_out must be 16-byte aligned, the scale
- * arrays 4-byte aligned; out and gate_up_out must not overlap each other or
- * any input.  Codes that encode NaN or infinity, the scale byte 255 (NaN) and
+ *   workspace      device pointer, 16-byte aligned, at least
+ *                  situ_glu_grouped_fwd_mxfp8_workspace_bytes(rows, hidden,
+ *                  experts, intermediate) bytes, owned by the caller: the
+ *                  call first rewrites both scale arrays there stage-major
+ *                  (a row's 4 scale bytes of each 128-wide slice of the
+ *                  hidden axis, rows contiguous), the layout the matrix-core
+ *                  kernel reads; its contents afterwards are unspecified
+ *   workspace_bytes  its size
+ * rows * hidden / 128 and experts * 2 * intermediate * hidden / 128 must be
+ * below 2^30 (else SITU_ERR_UNSUPPORTED).  x_codes, w_codes, out,
+ * gate_up_out and workspace must be 16-byte aligned, the scale arrays 4-byte
+ * aligned; out, gate_up_out and workspace must not overlap each other or any
+ * input.  Codes that encode NaN or infinity, the scale byte 255 (NaN) and
  * scale pairs whose products leave the fp32 range give unspecified values in
  * the rows and columns they reach.  Results are bitwise reproducible.
- * Returns as situ_glu_grouped_fwd; an unknown fp8_format is
- * SITU_ERR_INVALID_ARG.
+ * Returns as situ_glu_grouped_fwd; an unknown fp8_format, or a workspace that
+ * is NULL, too small or misaligned, is SITU_ERR_INVALID_ARG.
  */
 int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales,
                                int64_t rows, int64_t hidden,
@@ -358,7 +368,19 @@ int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales,
                                const void *routing_weights, int rw_dtype,
                                int64_t rw_rows, double beta,
                                const double *linear_beta, void *out,
-                               void *gate_up_out, void *stream);
+                               void *gate_up_out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace situ_glu_grouped_fwd_mxfp8 needs for these sizes: the
+ * two stage-major scale arrays, (rows + experts * 2 * intermediate) *
+ * hidden / 32 bytes, each rounded up to a multiple of 256.  Host only.
+ * Returns 0 for negative sizes or sizes beyond the SITU_GROUPED_MAX_* limits.
+ */
+size_t situ_glu_grouped_fwd_mxfp8_workspace_bytes(int64_t rows,
+                                                  int64_t hidden,
+                                                  int64_t experts,
+                                                  int64_t intermediate);
 
 /* Message describing the last error on the calling thread ("" if none). */
 const char *situ_glu_last_error(void);

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 5
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 6
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -240,18 +240,22 @@ def _grouped_mx(lib, **kw):
     lb = ctypes.c_double(25.0)
     a = dict(x=FAKE, xs=FAKE + 1024, rows=4, hidden=128, w=FAKE + 4096, ws=FAKE + 69632, experts=2, inter=128,
              fmt=0, off=FAKE + 71680, rw=FAKE + 71696, rwd=0, rw_rows=4, beta=4.0, lb=ctypes.byref(lb),
-             out=FAKE + 73728, gu=FAKE + 81920)
+             out=FAKE + 73728, gu=FAKE + 81920, wk=FAKE + 86016, wkb=4096)
     a.update(kw)
     return lib.situ_glu_grouped_fwd_mxfp8(a["x"], a["xs"], a["rows"], a["hidden"], a["w"], a["ws"], a["experts"],
                                           a["inter"], a["fmt"], a["off"], a["rw"], a["rwd"], a["rw_rows"],
-                                          a["beta"], a["lb"], a["out"], a["gu"], None)
+                                          a["beta"], a["lb"], a["out"], a["gu"], a["wk"], a["wkb"], None)
 
 
 # x codes 4 x 128 bytes at FAKE; x scales 16 bytes at FAKE + 1024; weight codes
 # 2 x 256 x 128 = 65536 bytes at FAKE + 4096; weight scales 2048 bytes at
 # FAKE + 69632; offsets 12 bytes at FAKE + 71680; routing weights 16 bytes at
-# FAKE + 71696; out 1024 bytes at FAKE + 73728; gate_up 2048 bytes at FAKE + 81920
+# FAKE + 71696; out 1024 bytes at FAKE + 73728; gate_up 2048 bytes at FAKE + 81920;
+# workspace (needs 256 + 2048 bytes) at FAKE + 86016
 BAD_GROUPED_MX = [
+    dict(wk=None), dict(wkb=2303), dict(wk=FAKE + 86024),   # workspace NULL, too small, misaligned
+    dict(wk=FAKE + 81920 + 1024),                            # workspace overlaps gate_up_out
+    dict(wk=FAKE + 69632),                                   # workspace overlaps the weight scales
     dict(fmt=2), dict(fmt=-1), dict(rwd=3), dict(beta=0.0), dict(rows=-1), dict(experts=0), dict(rw_rows=3),
     dict(x=None), dict(xs=None), dict(w=None), dict(ws=None), dict(off=None), dict(out=None),
     dict(x=FAKE + 8), dict(w=FAKE + 4104), dict(xs=FAKE + 1026), dict(ws=FAKE + 69634), dict(out=FAKE + 73736),
@@ -275,6 +279,19 @@ def test_grouped_mx_empty_and_unsupported(lib, capi):
     assert _grouped_mx(lib, hidden=192) == capi.SITU_ERR_UNSUPPORTED
     assert _grouped_mx(lib, inter=192) == capi.SITU_ERR_UNSUPPORTED
     assert _grouped_mx(lib, rows=(1 << 31) - 1, rw_rows=1, inter=1 << 20) == capi.SITU_ERR_UNSUPPORTED
+    # rows * hidden / 128 must stay below 2^30 (the stage-major scale offsets)
+    assert _grouped_mx(lib, rows=1 << 24, rw_rows=1, hidden=128 * 64) == capi.SITU_ERR_UNSUPPORTED
+    # the workspace may be NULL on an empty call
+    assert _grouped_mx(lib, rows=0, rw_rows=0, x=None, xs=None, out=None, gu=None, wk=None, wkb=0) == capi.SITU_OK
+
+
+def test_grouped_mx_workspace_bytes(lib, capi):
+    f = lib.situ_glu_grouped_fwd_mxfp8_workspace_bytes
+    # (rows + experts * 2I) * hidden / 32 bytes, each part rounded up to 256
+    assert f(4, 128, 2, 128) == 256 + 2048
+    assert f(65536, 7168, 16, 2048) == 65536 * 224 + 16 * 4096 * 224
+    assert f(0, 7168, 16, 2048) == 16 * 4096 * 224
+    assert f(-1, 128, 1, 128) == 0 and f(4, 128, capi.SITU_GROUPED_MAX_EXPERTS + 1, 128) == 0
 
 
 def test_grouped_mx_python_layer_rejects():
