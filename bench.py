@@ -365,7 +365,10 @@ def bench_grouped(args) -> int:
         "pct_of_peak": round(100.0 * value / peak, 2),
         "rows_per_s": round(w.rows / (ms / 1e3), 1),
         "kernels": kernels,
-        "roofline": {"bound": "mfma", "kernel": "situ_glu_grouped_fwd_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma",
+                     "kernel": ("situ_glu_grouped_fwd_kernel, with the two situ_mx_scales_stage_major_kernel "
+                                "launches of the same call" if mx else "situ_glu_grouped_fwd_kernel"),
+                     "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": _traffic(args.workload, "grouped", GEMM_KERNEL_SOURCE)},
         "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline_grouped(args.workload,

@@ -658,10 +658,11 @@ int grouped_fwd(int op, const void *x, const void *x_scales, int64_t rows, int64
     if (!weight || !group_offsets || !out)
         return fail(SITU_ERR_INVALID_ARG, "weight, group_offsets or out is NULL");
     const int64_t nk = hidden / 128, wrows = experts * 2 * intermediate;
-    if (op && (rows * nk >= ((int64_t)1 << 30) || wrows * nk >= ((int64_t)1 << 30)))
-        return fail(SITU_ERR_UNSUPPORTED, "rows * hidden / 128 and experts * 2 * intermediate * hidden / 128 must "
-                    "be below 2^30 on MXFP8 operands (got %lld and %lld)", (long long)(rows * nk),
-                    (long long)(wrows * nk));
+    const int64_t xst = situ::grouped_mx_stage_stride(rows), wst = situ::grouped_mx_stage_stride(wrows);
+    if (op && (xst * nk >= ((int64_t)1 << 30) || wst * nk >= ((int64_t)1 << 30)))
+        return fail(SITU_ERR_UNSUPPORTED, "(rows + 64) * hidden / 128 and (experts * 2 * intermediate + 64) * "
+                    "hidden / 128 must be below 2^30 on MXFP8 operands (got %lld and %lld)",
+                    (long long)(xst * nk), (long long)(wst * nk));
     if (op && (!x_scales || !w_scales))
         return fail(SITU_ERR_INVALID_ARG, "x_scales or w_scales is NULL");
     const int64_t need = op ? situ::grouped_mx_scale_bytes(rows, hidden) + situ::grouped_mx_scale_bytes(wrows, hidden)

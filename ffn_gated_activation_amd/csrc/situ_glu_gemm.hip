@@ -63,6 +63,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // E8M0 scale byte per 32 values along the hidden axis).
 enum { OP_BF16 = 0, OP_E4M3 = 1, OP_E5M2 = 2 };
 
+// Stage stride (dwords) of a stage-major scale array of R rows: R rounded up
+// to a whole 128-byte line, plus one line, so that the stages of a tile's
+// rows do not all fall into the same L2 sets (an unpadded stride of 64 Ki
+// rows is 256 KiB).
+__host__ __device__ inline int64_t stage_stride(int64_t R) { return (R + 31) / 32 * 32 + 32; }
+
 constexpr int kBM = 256;               // rows of a tile
 constexpr int kBN = 128;               // output columns of a tile
 constexpr int kBK = 64;                // bf16 hidden elements per stage (two stage buffers)
@@ -228,13 +234,13 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     const int nk = hidden / kStageK;
     const rsrc_t rz = make_rsrc(xb, 0u);  // reads as zero: the padding stage of an odd count
     // fp8 scales, stage-major: the dword of row r for stage kt is at
-    // kt * R + r (R = rows for x, E * 2I for w; R * nk < 2^30, checked on the
-    // host, so byte offsets fit 32 bits).  The descriptors start at the
+    // kt * stage_stride(R) + r (R = rows for x, E * 2I for w; stage_stride(R)
+    // * nk < 2^30, checked on the host, so byte offsets fit 32 bits).  The descriptors start at the
     // tile's first row and end with the array: rows past the tile read other
     // rows' scales, which only multiply the zero codes of those rows
     // (results never stored)
-    const uint32_t sxs = (uint32_t)rows * 4u;
-    const uint32_t sws = (uint32_t)experts * 2u * (uint32_t)inter * 4u;
+    const uint32_t sxs = (uint32_t)stage_stride(rows) * 4u;
+    const uint32_t sws = (uint32_t)stage_stride((int64_t)experts * 2 * inter) * 4u;
     rsrc_t rsa = rz, rsg = rz, rsu = rz;
     if (F8) {
         const uint32_t xend = (uint32_t)nk * sxs, wend = (uint32_t)nk * sws;
@@ -525,7 +531,7 @@ constexpr int kTrTile = 64;
 
 __global__ __launch_bounds__(256) void situ_mx_scales_stage_major_kernel(const uint32_t *__restrict__ in,
                                                                          uint32_t *__restrict__ out, int64_t R,
-                                                                         int nk)
+                                                                         int nk, int64_t stride)
 {
     __shared__ uint32_t tile[kTrTile][kTrTile + 1];
     const int64_t r0 = (int64_t)blockIdx.x * kTrTile;
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(256) void situ_mx_scales_stage_major_kernel(const u
     for (int k = 0; k < kTrTile * kTrTile / 256; ++k) {
         const int idx = t + 256 * k, j = idx / kTrTile, i = idx % kTrTile;
         if (r0 + i < R && s0 + j < nk)
-            out[(int64_t)(s0 + j) * R + r0 + i] = tile[i][j];
+            out[(int64_t)(s0 + j) * stride + r0 + i] = tile[i][j];
     }
 }
 
@@ -552,7 +558,7 @@ int launch_stage_major(const void *in, void *out, int64_t R, int nk, hipStream_t
         return 0;
     const dim3 grid((unsigned)((R + kTrTile - 1) / kTrTile), (unsigned)((nk + kTrTile - 1) / kTrTile));
     hipLaunchKernelGGL(situ_mx_scales_stage_major_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), R, nk);
+                       static_cast<const uint32_t *>(in), static_cast<uint32_t *>(out), R, nk, stage_stride(R));
     return (int)hipGetLastError();
 }
 
@@ -576,7 +582,12 @@ GemmFn pick(bool lb, bool fast, bool gu)
 
 int64_t grouped_slots(int64_t rows, int64_t experts) { return rows / kBM + experts; }
 
-int64_t grouped_mx_scale_bytes(int64_t rows, int64_t hidden) { return (rows * (hidden / 128) * 4 + 255) / 256 * 256; }
+int64_t grouped_mx_stage_stride(int64_t rows) { return stage_stride(rows); }
+
+int64_t grouped_mx_scale_bytes(int64_t rows, int64_t hidden)
+{
+    return (stage_stride(rows) * (hidden / 128) * 4 + 255) / 256 * 256;
+}
 
 int64_t grouped_grid_blocks(int64_t rows, int64_t experts, int64_t inter)
 {

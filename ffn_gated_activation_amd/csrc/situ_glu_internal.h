@@ -157,7 +157,10 @@ struct GroupedLaunch {
     UpK uk;
     void *workspace;      // fp8: stage-major scales (see above)
 };
-// Bytes of one stage-major scale array of `rows` rows (256-byte multiple).
+// Stage-major scales: the stage stride in dwords of an array of `rows` rows
+// (rows rounded up to a 128-byte line, plus one line), and the bytes of the
+// whole array (a 256-byte multiple).
+int64_t grouped_mx_stage_stride(int64_t rows);
 int64_t grouped_mx_scale_bytes(int64_t rows, int64_t hidden);
 // Row-tile slots of the grouped GEMM grid (floor(rows / 256) + experts) and
 // the workgroups of its launch.

@@ -350,8 +350,8 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows,
  *                  hidden axis, rows contiguous), the layout the matrix-core
  *                  kernel reads; its contents afterwards are unspecified
  *   workspace_bytes  its size
- * rows * hidden / 128 and experts * 2 * intermediate * hidden / 128 must be
- * below 2^30 (else SITU_ERR_UNSUPPORTED).  x_codes, w_codes, out,
+ * (rows + 64) * hidden / 128 and (experts * 2 * intermediate + 64) *
+ * hidden / 128 must be below 2^30 (else SITU_ERR_UNSUPPORTED).  x_codes, w_codes, out,
  * gate_up_out and workspace must be 16-byte aligned, the scale arrays 4-byte
  * aligned; out, gate_up_out and workspace must not overlap each other or any
  * input.  Codes that encode NaN or infinity, the scale byte 255 (NaN) and
@@ -373,8 +373,11 @@ int situ_glu_grouped_fwd_mxfp8(const void *x_codes, const void *x_scales,
 
 /*
  * Bytes of workspace situ_glu_grouped_fwd_mxfp8 needs for these sizes: the
- * two stage-major scale arrays, (rows + experts * 2 * intermediate) *
- * hidden / 32 bytes, each rounded up to a multiple of 256.  Host only.
+ * two stage-major scale arrays, each of hidden / 128 slices of R' dwords,
+ * where R' is its row count (rows, or experts * 2 * intermediate) rounded up
+ * to a multiple of 32 plus 32 (the padding keeps successive slices off the
+ * same cache sets), each array rounded up to a multiple of 256 bytes.  Host
+ * only.
  * Returns 0 for negative sizes or sizes beyond the SITU_GROUPED_MAX_* limits.
  */
 size_t situ_glu_grouped_fwd_mxfp8_workspace_bytes(int64_t rows,

@@ -251,9 +251,9 @@ def _grouped_mx(lib, **kw):
 # 2 x 256 x 128 = 65536 bytes at FAKE + 4096; weight scales 2048 bytes at
 # FAKE + 69632; offsets 12 bytes at FAKE + 71680; routing weights 16 bytes at
 # FAKE + 71696; out 1024 bytes at FAKE + 73728; gate_up 2048 bytes at FAKE + 81920;
-# workspace (needs 256 + 2048 bytes) at FAKE + 86016
+# workspace (needs 256 + 2304 bytes) at FAKE + 86016
 BAD_GROUPED_MX = [
-    dict(wk=None), dict(wkb=2303), dict(wk=FAKE + 86024),   # workspace NULL, too small, misaligned
+    dict(wk=None), dict(wkb=2559), dict(wk=FAKE + 86024),   # workspace NULL, too small, misaligned
     dict(wk=FAKE + 81920 + 1024),                            # workspace overlaps gate_up_out
     dict(wk=FAKE + 69632),                                   # workspace overlaps the weight scales
     dict(fmt=2), dict(fmt=-1), dict(rwd=3), dict(beta=0.0), dict(rows=-1), dict(experts=0), dict(rw_rows=3),
@@ -287,10 +287,10 @@ def test_grouped_mx_empty_and_unsupported(lib, capi):
 
 def test_grouped_mx_workspace_bytes(lib, capi):
     f = lib.situ_glu_grouped_fwd_mxfp8_workspace_bytes
-    # (rows + experts * 2I) * hidden / 32 bytes, each part rounded up to 256
-    assert f(4, 128, 2, 128) == 256 + 2048
-    assert f(65536, 7168, 16, 2048) == 65536 * 224 + 16 * 4096 * 224
-    assert f(0, 7168, 16, 2048) == 16 * 4096 * 224
+    # hidden / 128 slices of (R rounded up to 32, plus 32) dwords per array, each array rounded up to 256 bytes
+    assert f(4, 128, 2, 128) == 256 + 2304
+    assert f(65536, 7168, 16, 2048) == 2 * 56 * (65536 + 32) * 4
+    assert f(0, 7168, 16, 2048) == 56 * 32 * 4 + 56 * (65536 + 32) * 4
     assert f(-1, 128, 1, 128) == 0 and f(4, 128, capi.SITU_GROUPED_MAX_EXPERTS + 1, 128) == 0
 
 
