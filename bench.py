@@ -302,11 +302,16 @@ def bench_grouped(args) -> int:
     out = torch.empty(w.rows, w.inter, dtype=torch.bfloat16, device=dev)
     gu = torch.empty(w.rows, 2 * w.inter, dtype=torch.bfloat16, device=dev)
 
+    if mx:
+        from ffn_gated_activation_amd import situ_glu_grouped_fwd_mxfp8_workspace_bytes
+        wk = torch.empty(situ_glu_grouped_fwd_mxfp8_workspace_bytes(w.rows, w.hidden, w.experts, w.inter),
+                         dtype=torch.uint8, device=dev)
+
     def step(with_gu=False):
         if mx:
             situ_glu_grouped_fwd_mxfp8(x["x_codes"], x["x_scales"], x["weight_codes"], x["weight_scales"], off,
                                        x["routing_weights"], "e4m3", w.beta, w.linear_beta, out=out,
-                                       gate_up_out=gu if with_gu else None)
+                                       gate_up_out=gu if with_gu else None, workspace=wk)
         else:
             situ_glu_grouped_fwd(x["x"], x["weight"], off, x["routing_weights"], w.beta, w.linear_beta, out=out,
                                  gate_up_out=gu if with_gu else None)
