@@ -177,3 +177,27 @@ def test_grouped_mx_nan_scale_does_not_leak():
     err = np.abs(y - ref["out"])
     bad = keep & ~(err <= bound)
     assert not bad.any(), f"{int(bad.sum())} outputs outside the bound, first at {np.argwhere(bad)[0]}"
+
+
+def test_grouped_mx_explicit_workspace():
+    """A caller-provided workspace gives the same bits as the one allocated by
+    the binding; one byte too small is rejected before any launch."""
+    from ffn_gated_activation_amd import SituGluError, situ_glu_grouped_fwd_mxfp8_workspace_bytes
+    rows, experts, hidden, inter = 700, 3, 384, 256
+    inp = make_grouped_mx_inputs(rows, experts, hidden, inter, "e4m3", seed=31, rw_mode="uniform")
+    need = situ_glu_grouped_fwd_mxfp8_workspace_bytes(rows, hidden, experts, inter)
+    ref = _run(inp, 4.0, 25.0)
+    d = lambda t: t.to(DEV)  # noqa: E731
+    off = torch.tensor(inp["offsets"], dtype=torch.int32, device=DEV)
+    args = (d(inp["x_codes"]), d(inp["x_scales"]), d(inp["weight_codes"]), d(inp["weight_scales"]), off,
+            d(inp["routing_weights"]), "e4m3", 4.0, 25.0)
+    wk = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)     # stale contents must not matter
+    out = situ_glu_grouped_fwd_mxfp8(*args, workspace=wk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    small = torch.empty(need - 1, dtype=torch.uint8, device=DEV)
+    keep = torch.full((rows, inter), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(SituGluError):
+        situ_glu_grouped_fwd_mxfp8(*args, out=keep, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.all(keep == 3.0)
