@@ -336,6 +336,29 @@ def bench_grouped(args) -> int:
     k_ms = events(step, args.steps)
     gu_ms = events(lambda: step(True), max(1, args.steps // 4))
     kernels = {"grouped_fwd": {"ms": round(k_ms, 5)}, "grouped_fwd_with_gate_up": {"ms": round(gu_ms, 5)}}
+    if args.compare_unfused and mx:
+        # context only: the library's block-scaled fp8 GEMM (torch._scaled_mm with E8M0 scales per 32
+        # values) on one dense product of the same FLOPs, [M, K] x [K, 2I] with expert 0's weight, the
+        # workload's own codes and scales; then the stand-alone activation kernel on its [M, 2I] output
+        from ffn_gated_activation_amd import situ_glu_fwd
+        e8 = torch.float8_e8m0fnu
+        xa = x["x_codes"].view(torch.float8_e4m3fn)
+        wb = x["weight_codes"][0].view(torch.float8_e4m3fn)
+        sa, sb = x["x_scales"].view(e8), x["weight_scales"][0].contiguous().view(e8)
+        rw2 = x["routing_weights"].reshape(-1, 1)
+
+        def lib_mx():
+            return torch._scaled_mm(xa, wb.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+
+        def unfused():
+            situ_glu_fwd(lib_mx(), rw2, w.beta, w.linear_beta, out=out)
+        try:
+            for _ in range(5):
+                unfused()
+            kernels["library_mx_gemm_same_flops"] = {"ms": round(events(lib_mx, 20), 5)}
+            kernels["library_mx_gemm_then_activation"] = {"ms": round(events(unfused, 20), 5)}
+        except (RuntimeError, TypeError, AttributeError) as ex:
+            kernels["library_mx_gemm_same_flops"] = {"unavailable": f"{type(ex).__name__}: {str(ex)[:120]}"}
     if args.compare_unfused and not mx:
         # context only: the library grouped GEMM (torch._grouped_mm) writing gate_up, then the
         # stand-alone activation kernel on it
@@ -357,7 +380,8 @@ def bench_grouped(args) -> int:
     value = flops / (ms / 1e3) / 1e12
     achieved = flops / (k_ms / 1e3) / 1e12
     for k in kernels.values():
-        k["TFLOP/s"] = round(flops / (k["ms"] / 1e3) / 1e12, 2)
+        if "ms" in k:
+            k["TFLOP/s"] = round(flops / (k["ms"] / 1e3) / 1e12, 2)
     prec = "MXFP8 (E4M3)" if mx else "bf16"
     rec = {
         "metric": f"fused FC1 grouped GEMM + SiTU-GLU achieved TFLOP/s (% of MI355X {prec} dense peak) and rows/s",
@@ -397,7 +421,9 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-sample-rows-gemm", type=int, default=65536,
                     help="rows of the CPU-oracle sample of the grouped GEMM workload")
     ap.add_argument("--compare-unfused", action="store_true",
-                    help="grouped GEMM workload: also time torch._grouped_mm + the activation kernel (context)")
+                    help="grouped GEMM workloads: also time the library GEMM (torch._grouped_mm for bf16, "
+                         "torch._scaled_mm with MX scales on the same FLOPs for MXFP8) + the activation kernel "
+                         "(context)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache medians and the plain-kernel ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
