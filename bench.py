@@ -99,11 +99,16 @@ def _cpu_baseline(workload: str, sample_rows: int) -> dict:
     if mx:
         oracle.mx_quantize(y, mx, "floor", threads=cores)
     if go is not None:
-        oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"],
-                        want_scales=False, threads=cores)
+        bw = oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"],
+                             want_scales=False, threads=cores)
+        if mx:
+            inter = gu.shape[1] // 2
+            oracle.mx_quantize(bw["d_gate_up"][:, :inter], mx, "floor", threads=cores)
+            oracle.mx_quantize(bw["d_gate_up"][:, inter:], mx, "floor", threads=cores)
     dt = time.perf_counter() - t0
     b = algorithmic_bytes(workload, rows=sample_rows)["total"]
-    what = ("fp64 forward + MXFP8 quantisation" if mx else
+    what = ("fp64 forward+backward + MXFP8 quantisation of Y, dG and dU" if mx and go is not None else
+            "fp64 forward + MXFP8 quantisation" if mx else
             "fp64 forward+backward" if go is not None else "fp64 forward")
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{workload} recipe, first {sample_rows} rows (seed 0, drawn on the host), "
@@ -444,7 +449,7 @@ def main(argv=None) -> int:
             return 2
         return bench_attn_res(args) if args.workload in ATTN_RES else bench_grouped(args)
 
-    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_fwd, situ_glu_fwd_mxfp8
+    from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_bwd_mxfp8, situ_glu_fwd, situ_glu_fwd_mxfp8
     from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
 
     if not torch.cuda.is_available():
@@ -461,7 +466,10 @@ def main(argv=None) -> int:
         scales = torch.empty(w.rows, -(-w.inter // 32), dtype=torch.uint8, device=dev)
     else:
         y = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
-    dgu = torch.empty_like(gu) if w.backward else None
+    dgu = torch.empty_like(gu) if w.backward and not w.mx else None
+    if w.backward and w.mx:
+        dcodes = torch.empty(w.rows, 2 * w.inter, dtype=torch.uint8, device=dev)
+        dscales = torch.empty(w.rows, 2 * -(-w.inter // 32), dtype=torch.uint8, device=dev)
     drw = torch.empty_like(rw) if want else None
     torch.cuda.synchronize()
 
@@ -472,7 +480,11 @@ def main(argv=None) -> int:
             situ_glu_fwd(gu, rw, beta, lb, out=y)
 
     def bwd():
-        situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
+        if w.mx:
+            situ_glu_bwd_mxfp8(gu, rw, go, beta, lb, want, w.mx, "floor", d_codes=dcodes, d_scales=dscales,
+                               d_routing_weights=drw)
+        else:
+            situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
 
     def step():
         fwd()
@@ -505,6 +517,36 @@ def main(argv=None) -> int:
     fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
     bwd_ms = ev[1].elapsed_time(ev[2]) / args.steps if w.backward else 0.0
 
+    unfused = {}
+    if w.mx:
+        # context: the bf16 kernels followed by the stand-alone MXFP8 quantiser (same blocks and rounding;
+        # with I a multiple of 32 one quantiser call over [rows, 2I] gives d_gate_up's layout)
+        from ffn_gated_activation_amd import situ_glu_mx_quantize
+        yb = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+        def fwd_unfused():
+            situ_glu_fwd(gu, rw, beta, lb, out=yb)
+            situ_glu_mx_quantize(yb, w.mx, "floor", codes=codes, scales=scales)
+        fns = {"unfused_fwd_then_quantize": fwd_unfused}
+        if w.backward and w.inter % 32 == 0:
+            dgb = torch.empty_like(gu)
+
+            def bwd_unfused():
+                situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgb, d_routing_weights=drw)
+                situ_glu_mx_quantize(dgb, w.mx, "floor", codes=dcodes, scales=dscales)
+            fns["unfused_bwd_then_quantize"] = bwd_unfused
+        for name, fn in fns.items():
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            ev2[0].record()
+            for _ in range(args.steps):
+                fn()
+            ev2[1].record()
+            torch.cuda.synchronize()
+            unfused[name] = {"ms": round(ev2[0].elapsed_time(ev2[1]) / args.steps, 5)}
+
     _copy_calibration(args, dev)
 
     ab = algorithmic_bytes(args.workload)
@@ -518,9 +560,9 @@ def main(argv=None) -> int:
     dom_bytes = ab[dom]
     dom_ms = bwd_ms if w.backward else fwd_ms
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    kname = ("situ_glu_bwd_kernel" if w.backward else
+    kname = ("situ_glu_bwd_mx_kernel" if w.backward and w.mx else "situ_glu_bwd_kernel" if w.backward else
              "situ_glu_fwd_mx_kernel" if w.mx else "situ_glu_fwd_kernel")
-    src = MX_KERNEL_SOURCE if (w.mx and not w.backward) else KERNEL_SOURCE
+    src = MX_KERNEL_SOURCE if w.mx else KERNEL_SOURCE
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -536,7 +578,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rows": w.rows,
                    "intermediate": w.inter, "beta": w.beta, "linear_beta": w.linear_beta,
-                   "passes": ("fwd+bwd" + ("+d_routing_weights" if want else "") if w.backward else
+                   "passes": ("fwd+bwd" + ("+d_routing_weights" if want else "") +
+                              (f" (MXFP8 {w.mx} Y and d_gate_up)" if w.mx else "") if w.backward else
                               f"fwd (MXFP8 {w.mx} output)" if w.mx else "fwd"),
                    "algorithmic_bytes_per_step": ab["total"]},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -546,6 +589,7 @@ def main(argv=None) -> int:
                     "GB/s": round(ab["fwd"] / (fwd_ms / 1e3) / 1e9, 2)},
             "bwd": ({"ms": round(bwd_ms, 5), "bytes": ab["bwd"],
                      "GB/s": round(ab["bwd"] / (bwd_ms / 1e3) / 1e9, 2)} if w.backward else None),
+            **unfused,
         },
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -11,6 +11,7 @@ from .situ_glu import (  # noqa: F401
     situ_glu_abi_version,
     situ_glu_attn_res_fwd,
     situ_glu_bwd,
+    situ_glu_bwd_mxfp8,
     situ_glu_bwd_workspace_bytes,
     situ_glu_fwd,
     situ_glu_fwd_mxfp8,
@@ -24,7 +25,7 @@ from .situ_glu import (  # noqa: F401
 from ._capi import SituGluError  # noqa: F401
 from .autograd import WeightedSiTUFunction, weighted_situ  # noqa: F401
 
-__all__ = ["situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes", "situ_glu_last_error",
+__all__ = ["situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_mxfp8", "situ_glu_bwd_workspace_bytes", "situ_glu_last_error",
            "situ_glu_abi_version", "situ_glu_gate_window", "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize",
            "situ_glu_attn_res_fwd", "attn_res_core", "apply_attn_res", "situ_glu_grouped_fwd",
            "situ_glu_grouped_fwd_mxfp8",

@@ -501,6 +501,91 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t 
     return SITU_OK;
 }
 
+int situ_glu_bwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                       const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                       const double *linear_beta, const void *grad_out, int fp8_format, int scale_mode,
+                       void *d_codes, void *d_scales, void *d_routing_weights, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    g_last_error.clear();
+    int rc = check_common(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows,
+                          beta, linear_beta);
+    if (rc)
+        return rc;
+    if ((rc = check_mx(fp8_format, scale_mode)))
+        return rc;
+    const int64_t es = dtype_bytes(io_dtype);
+    const int64_t rs = dtype_bytes(rw_dtype);
+    if (d_routing_weights && reinterpret_cast<uintptr_t>(d_routing_weights) % rs)
+        return fail(SITU_ERR_INVALID_ARG, "d_routing_weights is not aligned to its element size");
+    if (rows == 0 || intermediate == 0) {
+        if (d_routing_weights && rw_rows > 0) {
+            const int err = situ::launch_zero(d_routing_weights, rw_rows * rs, stream);
+            if (err)
+                return fail(SITU_ERR_DEVICE, "zero fill failed: %s", situ::device_error_string(err));
+        }
+        return SITU_OK;
+    }
+    if (!grad_out)
+        return fail(SITU_ERR_INVALID_ARG, "grad_out is NULL");
+    if (!d_codes || !d_scales)
+        return fail(SITU_ERR_INVALID_ARG, "d_codes or d_scales is NULL");
+    if (reinterpret_cast<uintptr_t>(grad_out) % es)
+        return fail(SITU_ERR_INVALID_ARG, "grad_out is not aligned to its element size");
+    const bool broadcast_dr = d_routing_weights && rw_rows == 1 && rows > 1;
+    const size_t need = broadcast_dr ? (size_t)rows * sizeof(float) : 0;
+    if (need) {
+        if (!workspace)
+            return fail(SITU_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
+        if (workspace_bytes < need)
+            return fail(SITU_ERR_INVALID_ARG, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+        if (reinterpret_cast<uintptr_t>(workspace) % sizeof(float))
+            return fail(SITU_ERR_INVALID_ARG, "workspace is not 4-byte aligned");
+    }
+    const Range ins[] = {range("gate_up", gate_up, rows * intermediate * 2 * es),
+                         range("routing_weights", routing_weights, rw_rows * rs),
+                         range("grad_out", grad_out, rows * intermediate * es)};
+    const Range outs[] = {range("d_codes", d_codes, rows * intermediate * 2),
+                          range("d_scales", d_scales, rows * 2 * mx_blocks(intermediate)),
+                          range("d_routing_weights", d_routing_weights, d_routing_weights ? rw_rows * rs : 0),
+                          range("workspace", workspace, (int64_t)need)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return fail(SITU_ERR_INVALID_ARG, "%s overlaps input %s", o.name, i.name);
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], outs[b]))
+                return fail(SITU_ERR_INVALID_ARG, "%s overlaps %s", outs[a].name, outs[b].name);
+
+    situ::BwdMxLaunch L{};
+    L.gate_up = gate_up;
+    L.rw = routing_weights;
+    L.rw_bf16 = rw_dtype == SITU_DTYPE_BF16;
+    L.rw_stride = rw_rows == rows ? 1 : 0;
+    L.grad_out = grad_out;
+    L.codes = d_codes;
+    L.scales = d_scales;
+    L.d_rw = d_routing_weights;
+    L.row_partials = static_cast<float *>(need ? workspace : nullptr);
+    L.rows = rows;
+    L.inter = (int)intermediate;
+    L.io = io_dtype == SITU_DTYPE_BF16 ? situ::IO_BF16 : situ::IO_F32;
+    L.vec = aligned16(gate_up) && aligned16(grad_out) && (intermediate * es) % 16 == 0 &&
+            intermediate * 2 * es < ((int64_t)1 << 31) && aligned_to(d_codes, io_dtype == SITU_DTYPE_BF16 ? 8 : 4);
+    L.lb = linear_beta != nullptr;
+    L.fast = beta == 4.0;
+    L.fmt = fp8_format == SITU_FP8_E5M2 ? situ::FP8_E5M2 : situ::FP8_E4M3;
+    L.ceil_mode = scale_mode == SITU_MX_SCALE_CEIL;
+    L.rows_per_block = rows_per_block_override();
+    L.gk = gate_consts(beta);
+    L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
+    const int err = situ::launch_bwd_mx(L, stream);
+    if (err)
+        return fail(SITU_ERR_DEVICE, "MXFP8 backward launch failed: %s", situ::device_error_string(err));
+    return SITU_OK;
+}
+
 int situ_glu_mx_quantize(const void *x, int io_dtype, int64_t rows, int64_t cols, int fp8_format,
                          int scale_mode, void *codes, void *scales, void *stream)
 {

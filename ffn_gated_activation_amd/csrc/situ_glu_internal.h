@@ -95,6 +95,31 @@ struct FwdMxLaunch {
     UpK uk;
 };
 
+// Backward with MXFP8 d_gate_up: codes [rows, 2 inter] bytes (dG, then dU),
+// scales [rows, 2 ceil(inter / 32)] bytes (dG's blocks, then dU's).
+struct BwdMxLaunch {
+    const void *gate_up;
+    const void *rw;
+    int rw_bf16;
+    int64_t rw_stride;
+    const void *grad_out;
+    void *codes;
+    void *scales;
+    void *d_rw;           // NULL: no routing-weight gradient
+    float *row_partials;  // workspace, [rows] fp32, used when rw_stride == 0 and d_rw
+    int64_t rows;
+    int inter;
+    int io;
+    int vec;              // 1: 128-bit loads, 8-byte (bf16) / 4-byte (fp32) code stores
+    int lb;
+    int fast;
+    int fmt;
+    int ceil_mode;
+    int rows_per_block;
+    GateK gk;
+    UpK uk;
+};
+
 // MXFP8 quantisation of x [rows, cols] (io dtype).
 struct MxQuantLaunch {
     const void *x;
@@ -175,7 +200,11 @@ int attn_res_path(int io, int hidden, int nb, int vec_ok);
 int launch_fwd(const FwdLaunch &L, void *stream);
 int launch_bwd(const BwdLaunch &L, void *stream);
 int launch_fwd_mx(const FwdMxLaunch &L, void *stream);
+int launch_bwd_mx(const BwdMxLaunch &L, void *stream);
 int launch_mx_quant(const MxQuantLaunch &L, void *stream);
+// Fixed-order sum of the [rows] fp32 partials into the one routing-weight
+// gradient (broadcast weight).
+int launch_dr_reduce(const float *row_partials, int64_t rows, void *d_rw, int rw_bf16, void *stream);
 int launch_attn_res(const AresLaunch &L, void *stream);
 int launch_grouped_fwd(const GroupedLaunch &L, void *stream);
 // Zero `bytes` bytes at device pointer p with a fill kernel.

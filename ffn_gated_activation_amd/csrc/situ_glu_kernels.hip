@@ -328,12 +328,16 @@ int launch_bwd(const BwdLaunch &L, void *stream)
                        L.rw_stride, L.grad_out, L.d_gate_up, L.d_rw, L.row_partials, L.rows, L.inter,
                        sh.waves_per_row, L.gk, L.uk);
     int err = (int)hipGetLastError();
-    if (err == 0 && dr && L.rw_stride == 0) {
-        hipLaunchKernelGGL(situ_glu_dr_reduce_kernel, dim3(1), dim3(kReduceBlock), 0, (hipStream_t)stream,
-                           (const float *)L.row_partials, L.rows, L.d_rw, L.rw_bf16);
-        err = (int)hipGetLastError();
-    }
+    if (err == 0 && dr && L.rw_stride == 0)
+        err = launch_dr_reduce(L.row_partials, L.rows, L.d_rw, L.rw_bf16, stream);
     return err;
+}
+
+int launch_dr_reduce(const float *row_partials, int64_t rows, void *d_rw, int rw_bf16, void *stream)
+{
+    hipLaunchKernelGGL(situ_glu_dr_reduce_kernel, dim3(1), dim3(kReduceBlock), 0, (hipStream_t)stream,
+                       row_partials, rows, d_rw, rw_bf16);
+    return (int)hipGetLastError();
 }
 
 int launch_zero(void *p, int64_t bytes, void *stream)

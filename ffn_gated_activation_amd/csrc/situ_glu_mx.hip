@@ -334,11 +334,164 @@ situ_glu_mx_quant_elem_kernel(const void *__restrict__ x, unsigned char *__restr
     }
 }
 
+// Backward with MXFP8 d_gate_up: dG and dU of a row are quantised as two
+// rows of `inter` values (blocks never straddle them): codes [rows, 2 inter]
+// (dG then dU), scales [rows, 2 ceil(inter / 32)] (dG's blocks, then dU's).
+// dr as in the bf16 backward; `d_rw` NULL skips it.  128-bit path with the
+// backward's placement and unroll.
+#ifndef SITU_UNROLL_BWD_MX
+#define SITU_UNROLL_BWD_MX 2
+#endif
+#ifndef SITU_BWD_MX_WAVES_PER_SIMD
+#define SITU_BWD_MX_WAVES_PER_SIMD 1
+#endif
+constexpr int kUnrollBwdMx = SITU_UNROLL_BWD_MX;
+
+template <int IO, bool LB, bool FAST, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves, SITU_BWD_MX_WAVES_PER_SIMD)
+situ_glu_bwd_mx_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
+                           int64_t rw_stride, const void *__restrict__ grad_out, unsigned char *__restrict__ codes,
+                           unsigned char *__restrict__ scales, void *__restrict__ d_rw,
+                           float *__restrict__ row_partials, int64_t rows, int inter, int waves_per_row, GateK gk,
+                           UpK uk)
+{
+    constexpr bool PRECISE = IO == IO_F32;
+    using T = Io<IO>;
+    constexpr int E = T::kPerVec;
+    constexpr int kStrip = 64 * kUnrollBwdMx;
+    __shared__ float wave_part[kMaxWaves];
+    const int lane = threadIdx.x & 63;
+    const Place pl = place(waves_per_row);
+    const bool live = pl.row < rows;
+    const bool dr = d_rw != nullptr;
+    float acc = 0.0f;
+    if (live) {
+        const int nv = inter / E;
+        const uint32_t half = (uint32_t)nv * 16u;
+        const int spr = (nv + kStrip - 1) / kStrip;
+        const int nblk = (inter + kMxBlock - 1) / kMxBlock;
+        const char *row = static_cast<const char *>(gate_up) + pl.row * (int64_t)half * 2;
+        const rsrc_t rg = make_rsrc(row, half), ru = make_rsrc(row + half, half);
+        const rsrc_t rgo = make_rsrc(static_cast<const char *>(grad_out) + pl.row * (int64_t)half, half);
+        unsigned char *crow = codes + pl.row * 2 * (int64_t)inter;
+        unsigned char *srow = scales + pl.row * 2 * (int64_t)nblk;
+        const rsrc_t rcg = make_rsrc(crow, (uint32_t)inter), rcu = make_rsrc(crow + inter, (uint32_t)inter);
+        const rsrc_t rsg = make_rsrc(srow, (uint32_t)nblk), rsu = make_rsrc(srow + nblk, (uint32_t)nblk);
+        const float r = load_rw(rw, rw_bf16, pl.row * rw_stride);
+        const float cG = LB ? 4.0f * r * uk.beta2 : 4.0f * r;
+        const float cU = LB ? 4.0f * r * gk.beta1 : r * gk.beta1;
+        for (int s = pl.strip0; s < spr; s += pl.wpr) {
+            uint4 gv[kUnrollBwdMx], uv[kUnrollBwdMx], ov[kUnrollBwdMx];
+#pragma unroll
+            for (int k = 0; k < kUnrollBwdMx; ++k) {
+                const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
+                gv[k] = bload(rg, off);
+                uv[k] = bload(ru, off);
+                ov[k] = bload(rgo, off);
+            }
+#pragma unroll
+            for (int k = 0; k < kUnrollBwdMx; ++k) {
+                // past the row end the loads returned zeros: dG = dU = 0
+                // there, which leaves every block maximum unchanged, and the
+                // stores are dropped
+                float g[E], u[E], og[E], dg[E], du[E];
+                T::unpack(gv[k], g);
+                T::unpack(uv[k], u);
+                T::unpack(ov[k], og);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const BwdOut b = bwd_elem<LB, FAST, PRECISE>(g[e], u[e], og[e], cG, cU, gk, uk);
+                    dg[e] = b.dg;
+                    du[e] = b.du;
+                    acc += b.p;
+                }
+                const int v = s * kStrip + 64 * k + lane;
+                quantize_vector<FMT, MODE, E>(dg, v, lane, rcg, rsg);
+                quantize_vector<FMT, MODE, E>(du, v, lane, rcu, rsu);
+            }
+        }
+    }
+    if (dr) {
+        const float scale = LB ? gk.beta1 * uk.beta2 : gk.beta1;
+        const float s = wave_sum(acc);
+        if (pl.wpr == 1) {
+            if (live && lane == 0)
+                write_row_dr(s * scale, pl.row, rw_stride, rw_bf16, d_rw, row_partials);
+        } else {
+            // the row's wavefronts meet in LDS; the first one adds them in order
+            if (lane == 0)
+                wave_part[pl.slot] = s;
+            __syncthreads();
+            if (live && pl.strip0 == 0 && lane == 0) {
+                float t = 0.0f;
+                for (int w = 0; w < pl.wpr; ++w)
+                    t += wave_part[pl.slot + w];
+                write_row_dr(t * scale, pl.row, rw_stride, rw_bf16, d_rw, row_partials);
+            }
+        }
+    }
+}
+
+// Backward with MXFP8 d_gate_up, element path (any alignment, any
+// intermediate): one wavefront per row, 64 values (two blocks) per step.
+template <int IO, bool LB, bool FAST, int FMT, int MODE>
+__global__ void __launch_bounds__(64 * kMaxWaves)
+situ_glu_bwd_mx_elem_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
+                            int64_t rw_stride, const void *__restrict__ grad_out, unsigned char *__restrict__ codes,
+                            unsigned char *__restrict__ scales, void *__restrict__ d_rw,
+                            float *__restrict__ row_partials, int64_t rows, int inter, int /*unused*/, GateK gk,
+                            UpK uk)
+{
+    constexpr bool PRECISE = IO == IO_F32;
+    using T = Io<IO>;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows)
+        return;
+    const int nblk = (inter + kMxBlock - 1) / kMxBlock;
+    const float r = load_rw(rw, rw_bf16, row * rw_stride);
+    const float cG = LB ? 4.0f * r * uk.beta2 : 4.0f * r;
+    const float cU = LB ? 4.0f * r * gk.beta1 : r * gk.beta1;
+    const char *gu_row = static_cast<const char *>(gate_up) + row * (int64_t)inter * 2 * T::kBytes;
+    const char *go_row = static_cast<const char *>(grad_out) + row * (int64_t)inter * T::kBytes;
+    unsigned char *cg_row = codes + row * 2 * (int64_t)inter, *cu_row = cg_row + inter;
+    unsigned char *sg_row = scales + row * 2 * (int64_t)nblk, *su_row = sg_row + nblk;
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < inter; j0 += 64) {
+        const int j = j0 + lane;
+        float dg = 0.0f, du = 0.0f;
+        if (j < inter) {
+            const BwdOut b = bwd_elem<LB, FAST, PRECISE>(T::load1(gu_row, j), T::load1(gu_row, (int64_t)inter + j),
+                                                         T::load1(go_row, j), cG, cU, gk, uk);
+            dg = b.dg;
+            du = b.du;
+            acc += b.p;
+        }
+        const uint32_t code_g = scale_code<FMT, MODE>(half_wave_max(__float_as_uint(dg) & 0x7fffffffu));
+        const uint32_t code_u = scale_code<FMT, MODE>(half_wave_max(__float_as_uint(du) & 0x7fffffffu));
+        if (j < inter) {
+            cg_row[j] = encode1<FMT, MODE>(dg, code_g);
+            cu_row[j] = encode1<FMT, MODE>(du, code_u);
+            if ((lane & 31) == 0) {
+                sg_row[j / kMxBlock] = (unsigned char)code_g;
+                su_row[j / kMxBlock] = (unsigned char)code_u;
+            }
+        }
+    }
+    if (d_rw != nullptr) {
+        const float s = wave_sum(acc);
+        if (lane == 0)
+            write_row_dr(s * (LB ? gk.beta1 * uk.beta2 : gk.beta1), row, rw_stride, rw_bf16, d_rw, row_partials);
+    }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 using FwdMxFn = void (*)(const void *, const void *, int, int64_t, unsigned char *, unsigned char *, int64_t, int,
                          int, GateK, UpK);
 using QuantFn = void (*)(const void *, unsigned char *, unsigned char *, int64_t, int, int);
+using BwdMxFn = void (*)(const void *, const void *, int, int64_t, const void *, unsigned char *, unsigned char *,
+                         void *, float *, int64_t, int, int, GateK, UpK);
 
 template <int IO, bool VEC, bool LB, bool FAST, int FMT, int MODE>
 constexpr FwdMxFn fwd_mx_fn()
@@ -367,6 +520,24 @@ const FwdMxFn kFwdMx[2][2][4][2][2] = {
     {SITU_MX_ROW(IO_F32, false), SITU_MX_ROW(IO_F32, true)},
     {SITU_MX_ROW(IO_BF16, false), SITU_MX_ROW(IO_BF16, true)},
 };
+template <int IO, bool VEC, bool LB, bool FAST, int FMT, int MODE>
+constexpr BwdMxFn bwd_mx_fn()
+{
+    if constexpr (VEC)
+        return situ_glu_bwd_mx_vec_kernel<IO, LB, FAST, FMT, MODE>;
+    else
+        return situ_glu_bwd_mx_elem_kernel<IO, LB, FAST, FMT, MODE>;
+}
+#define SITU_BMX_FM(IO, VEC, LB, FAST, FMT) {bwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_FLOOR>(), bwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_CEIL>()}
+#define SITU_BMX_CASE(IO, VEC, LB, FAST) {SITU_BMX_FM(IO, VEC, LB, FAST, FP8_E4M3), SITU_BMX_FM(IO, VEC, LB, FAST, FP8_E5M2)}
+#define SITU_BMX_ROW(IO, VEC)                                                                        \
+    { SITU_BMX_CASE(IO, VEC, false, false), SITU_BMX_CASE(IO, VEC, false, true),                    \
+      SITU_BMX_CASE(IO, VEC, true, false), SITU_BMX_CASE(IO, VEC, true, true) }
+// index: [io][vec][lb * 2 + fast][fmt][mode]
+const BwdMxFn kBwdMx[2][2][4][2][2] = {
+    {SITU_BMX_ROW(IO_F32, false), SITU_BMX_ROW(IO_F32, true)},
+    {SITU_BMX_ROW(IO_BF16, false), SITU_BMX_ROW(IO_BF16, true)},
+};
 #define SITU_Q_FM(IO, VEC, FMT) {quant_fn<IO, VEC, FMT, MX_FLOOR>(), quant_fn<IO, VEC, FMT, MX_CEIL>()}
 // index: [io][vec][fmt][mode]
 const QuantFn kQuant[2][2][2][2] = {
@@ -386,6 +557,19 @@ int launch_fwd_mx(const FwdMxLaunch &L, void *stream)
                        static_cast<unsigned char *>(L.codes), static_cast<unsigned char *>(L.scales), L.rows,
                        L.inter, sh.waves_per_row, L.gk, L.uk);
     return (int)hipGetLastError();
+}
+
+int launch_bwd_mx(const BwdMxLaunch &L, void *stream)
+{
+    const Shape sh = shape(L.rows, L.inter, L.io, L.vec, L.rows_per_block, kUnrollBwdMx);
+    const BwdMxFn fn = kBwdMx[L.io][L.vec][L.lb * 2 + L.fast][L.fmt][L.ceil_mode ? MX_CEIL : MX_FLOOR];
+    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up, L.rw, L.rw_bf16, L.rw_stride,
+                       L.grad_out, static_cast<unsigned char *>(L.codes), static_cast<unsigned char *>(L.scales),
+                       L.d_rw, L.row_partials, L.rows, L.inter, sh.waves_per_row, L.gk, L.uk);
+    int err = (int)hipGetLastError();
+    if (err == 0 && L.d_rw && L.rw_stride == 0)
+        err = launch_dr_reduce(L.row_partials, L.rows, L.d_rw, L.rw_bf16, stream);
+    return err;
 }
 
 int launch_mx_quant(const MxQuantLaunch &L, void *stream)

@@ -174,6 +174,54 @@ def situ_glu_fwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, bet
     return codes, scales
 
 
+def situ_glu_bwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, grad_out: torch.Tensor,
+                       beta: float = 4.0, linear_beta: float | None = 25.0, want_drw: bool = True,
+                       fp8_format: str = "e4m3", scale_mode: str = "floor", d_codes: torch.Tensor | None = None,
+                       d_scales: torch.Tensor | None = None, d_routing_weights: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None):
+    """Backward with MXFP8 d_gate_up: returns (d_codes uint8 [..., 2I],
+    d_scales uint8 [..., 2 ceil(I / 32)], d_routing_weights or None).
+
+    Per row, d_codes holds dG's codes then dU's, d_scales dG's block scales
+    then dU's (blocks of 32 along I, never mixing dG and dU); the value of
+    dG element j is code * 2^(d_scales[..., j // 32] - 127) and of dU element
+    j is code * 2^(d_scales[..., nblk + j // 32] - 127), nblk = ceil(I / 32).
+    """
+    lib = _capi.load()
+    _check_device(gate_up, routing_weights, grad_out, d_codes, d_scales, d_routing_weights, workspace)
+    io = _io_dtype(gate_up, "gate_up")
+    rwd = _io_dtype(routing_weights, "routing_weights")
+    fmt, mode = _mx_args(fp8_format, scale_mode)
+    lead, rows, inter, rw_rows = _flatten(gate_up, routing_weights)
+    if grad_out.dtype != gate_up.dtype or tuple(grad_out.shape) != lead + (inter,):
+        raise ValueError(f"grad_out must be {lead + (inter,)} of dtype {gate_up.dtype}")
+    if not grad_out.is_contiguous():
+        raise ValueError("grad_out must be contiguous")
+    nblk = -(-inter // _capi.SITU_MX_BLOCK)
+    if d_codes is None:
+        d_codes = torch.empty(lead + (2 * inter,), dtype=torch.uint8, device=gate_up.device)
+    elif d_codes.dtype != torch.uint8 or tuple(d_codes.shape) != lead + (2 * inter,) or not d_codes.is_contiguous():
+        raise ValueError(f"d_codes must be a contiguous uint8 tensor of shape {lead + (2 * inter,)}")
+    if d_scales is None:
+        d_scales = torch.empty(lead + (2 * nblk,), dtype=torch.uint8, device=gate_up.device)
+    elif d_scales.dtype != torch.uint8 or tuple(d_scales.shape) != lead + (2 * nblk,) or not d_scales.is_contiguous():
+        raise ValueError(f"d_scales must be a contiguous uint8 tensor of shape {lead + (2 * nblk,)}")
+    if want_drw and d_routing_weights is None:
+        d_routing_weights = torch.empty_like(routing_weights)
+    if not want_drw:
+        d_routing_weights = None
+    need = int(lib.situ_glu_bwd_workspace_bytes(rows, inter, rw_rows)) if want_drw else 0
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=gate_up.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    _capi.check(lib.situ_glu_bwd_mxfp8(
+        gate_up.data_ptr(), io, rows, inter, routing_weights.data_ptr(), rwd, rw_rows, float(beta),
+        _capi.lb_ptr(linear_beta), grad_out.data_ptr(), fmt, mode, d_codes.data_ptr(), d_scales.data_ptr(),
+        d_routing_weights.data_ptr() if d_routing_weights is not None else None, ws_ptr, ws_bytes, _stream()), lib)
+    return d_codes, d_scales, d_routing_weights
+
+
 def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: str = "floor",
                          codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """MXFP8 block quantisation of x [..., cols] (float32 or bfloat16) along its

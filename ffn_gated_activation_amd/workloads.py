@@ -34,6 +34,11 @@ torch's round-to-nearest-even; "N(0, s)" means s * randn):
                 the routed_top8 inputs (same draws), forward only, with the
                 output written as MXFP8 (E4M3 elements, 32-value blocks,
                 floor scale rule) instead of bf16.
+  routed_top8_mxfp8_train
+                the routed_top8 inputs (same draws, grad_out included),
+                forward + backward + d_routing_weights, with Y and d_gate_up
+                written as MXFP8 (E4M3, row-wise 32-value blocks of Y, dG and
+                dU, floor scale rule).
 
 Attention-residual mixing (make_attn_res_inputs; draws in the order stored
 sums -> prefix -> norm weight -> projection weight, fp32, then rounded):
@@ -110,8 +115,14 @@ WORKLOADS = {
     "routed_top8_mxfp8": Workload("routed_top8_mxfp8", 65536, 2048, torch.bfloat16, 4.0, 25.0, False, False,
                                   False, "routed_top8 inputs, forward only, output MXFP8 (E4M3, blocks of 32, "
                                   "E8M0 floor scales)", recipe="routed_top8", mx="e4m3"),
+    "routed_top8_mxfp8_train": Workload("routed_top8_mxfp8_train", 65536, 2048, torch.bfloat16, 4.0, 25.0, True,
+                                        True, False, "routed_top8 inputs, forward + backward + dr with the "
+                                        "forward's Y and the backward's d_gate_up written as MXFP8 (E4M3, "
+                                        "row-wise blocks of 32, E8M0 floor scales)", recipe="routed_top8",
+                                        mx="e4m3"),
 }
-ORDER = ["fp32_small", "top1_fwd", "dense_ffn", "routed_top8", "stress_sat", "routed_top8_mxfp8"]
+ORDER = ["fp32_small", "top1_fwd", "dense_ffn", "routed_top8", "stress_sat", "routed_top8_mxfp8",
+         "routed_top8_mxfp8_train"]
 
 
 def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
@@ -122,7 +133,9 @@ def make_inputs(name: str, device="cpu", seed: int = 0, rows: int | None = None,
     w = WORKLOADS[name]
     if w.recipe is not None:
         x = make_inputs(w.recipe, device, seed, rows, inter)
-        x.update(workload=w, grad_out=None, want_drw=False)
+        x.update(workload=w, want_drw=w.want_drw)
+        if not w.backward:
+            x.update(grad_out=None)
         return x
     rows = w.rows if rows is None else int(rows)
     if inter is not None:
@@ -178,7 +191,9 @@ def algorithmic_bytes(name: str, rows: int | None = None) -> dict:
 
     forward : gate_up + routing weights + out (MXFP8 output: one byte per
               value plus one scale byte per 32-value block)
-    backward: gate_up + routing weights + grad_out + d_gate_up (+ d_routing_weights)
+    backward: gate_up + routing weights + grad_out + d_gate_up (+ d_routing_weights);
+              d_gate_up as MXFP8 when the workload's outputs are: one byte per
+              value plus one scale byte per 32-value block of dG and of dU
     """
     w = WORKLOADS[name]
     rows = w.rows if rows is None else rows
@@ -188,7 +203,8 @@ def algorithmic_bytes(name: str, rows: int | None = None) -> dict:
     fwd = rows * 2 * w.inter * s + rw_bytes + out_bytes
     bwd = 0
     if w.backward:
-        bwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s + rows * 2 * w.inter * s
+        dgu_bytes = rows * 2 * (w.inter + -(-w.inter // 32)) if w.mx else rows * 2 * w.inter * s
+        bwd = rows * 2 * w.inter * s + rw_bytes + rows * w.inter * s + dgu_bytes
         if w.want_drw:
             bwd += rw_bytes
     return {"fwd": fwd, "bwd": bwd, "total": fwd + bwd}

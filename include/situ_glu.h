@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 6
+#define SITU_GLU_ABI_VERSION 7
 
 /* return codes */
 #define SITU_OK 0
@@ -189,6 +189,40 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows,
                        int rw_dtype, int64_t rw_rows, double beta,
                        const double *linear_beta, int fp8_format,
                        int scale_mode, void *codes, void *scales,
+                       void *stream);
+
+/*
+ * Backward with MXFP8 output: dG, dU and dr as situ_glu_bwd computes them
+ * (fp32, from the saved inputs), with d_gate_up written as MXFP8 blocks
+ * instead of io_dtype values — the form the next projection's gradient GEMM
+ * takes under the MXFP8 recipe in which the Megatron-LM PR "[Dev] Add
+ * SiTU-GLU through Transformer Engine" (section "Test results") runs the MoE
+ * forward and backward.  Blocks, scales and element rounding as for
+ * situ_glu_fwd_mxfp8, with dG and dU of a row quantised as two separate rows
+ * of `intermediate` values (a block never mixes them); blocks run along the
+ * intermediate axis (row-wise).
+ *
+ *   gate_up ... grad_out   as for situ_glu_bwd
+ *   fp8_format, scale_mode as for situ_glu_fwd_mxfp8
+ *   d_codes      device pointer, [rows, 2*intermediate] bytes: dG's codes,
+ *                then dU's, per row
+ *   d_scales     device pointer, [rows, 2*ceil(intermediate / 32)] bytes:
+ *                dG's block scales, then dU's, per row
+ *   d_routing_weights, workspace, workspace_bytes, stream   as for
+ *                situ_glu_bwd (situ_glu_bwd_workspace_bytes gives the size)
+ * Outputs must not overlap the inputs or each other.  Any alignment is
+ * accepted; 16-byte-aligned gate_up and grad_out with intermediate a
+ * multiple of 8 (bf16) or 4 (fp32) and d_codes aligned to 8 (bf16) or 4
+ * (fp32) bytes take the 128-bit path.  Returns as situ_glu_bwd; an unknown
+ * format or mode is SITU_ERR_INVALID_ARG.
+ */
+int situ_glu_bwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows,
+                       int64_t intermediate, const void *routing_weights,
+                       int rw_dtype, int64_t rw_rows, double beta,
+                       const double *linear_beta, const void *grad_out,
+                       int fp8_format, int scale_mode, void *d_codes,
+                       void *d_scales, void *d_routing_weights,
+                       void *workspace, size_t workspace_bytes,
                        void *stream);
 
 /*

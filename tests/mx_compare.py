@@ -51,6 +51,38 @@ def y_error_bound(gate_up64: np.ndarray, beta: float, linear_beta, io_bf16: bool
     return rel
 
 
+def _small_arg(y: np.ndarray) -> np.ndarray:
+    """Relative error of the bf16-io kernels' 1 - exp(-y): the first-order
+    replacement below y = 2^-11, cancellation above it."""
+    with np.errstate(divide="ignore"):
+        return np.where(y < 2.0 ** -11, 0.5 * y, 2.0 ** -23 / np.maximum(y, 2.0 ** -11))
+
+
+def grad_error_bounds(gate_up64: np.ndarray, dgu64: np.ndarray, dg_scale64: np.ndarray, beta: float, linear_beta,
+                      io_bf16: bool, window=None) -> tuple[np.ndarray, np.ndarray]:
+    """Absolute bounds on the backward's fp32 dG and dU (before any output
+    rounding).  fp32 io: the 1e-5 bar of the fp32 backward (dG relative to the
+    sum of the magnitudes of dT_g/dG's two terms, dg_scale).  bf16 io adds the
+    kernels' cheaper pieces: dG carries T_u and dU carries T_g, each with the
+    small-argument error of its 1 - exp(-y) (y = 2|U|/linear_beta, 2|G|/beta);
+    inside the window (G*_f32, half width) around the gate's minimum dT_g/dG
+    is a quadratic whose dropped term is below 1e-4 of the linear one, counted
+    here as 1e-4 dg_scale."""
+    inter = gate_up64.shape[1] // 2
+    G, U = gate_up64[:, :inter], gate_up64[:, inter:]
+    dG, dU = np.abs(dgu64[:, :inter]), np.abs(dgu64[:, inter:])
+    eg = F32_REL * dg_scale64
+    eu = F32_REL * dU
+    if io_bf16:
+        if linear_beta is not None:
+            eg = eg + _small_arg(2.0 * np.abs(U) / linear_beta) * dG
+        eu = eu + _small_arg(2.0 * np.abs(G) / beta) * dU
+        if window is not None:
+            g0, hw = window
+            eg = eg + np.where(np.abs(G - g0) <= hw, 1e-4 * dg_scale64, 0.0)
+    return eg, eu
+
+
 def _pad_blocks(a: np.ndarray, fill) -> np.ndarray:
     rows, cols = a.shape
     nblk = -(-cols // BLOCK)

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 6
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 7
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -105,6 +105,48 @@ def test_bwd_rejects(lib, capi, kw):
     rc = _bwd(lib, **kw)
     assert rc == capi.SITU_ERR_INVALID_ARG, (kw, rc)
     assert capi.last_error(lib) != ""
+
+
+def _bwd_mx(lib, **kw):
+    # gate_up 4 x 2 x 40 bf16 = 640 bytes at FAKE; rw at FAKE + 4096; grad_out 320 bytes at FAKE + 8192;
+    # d_codes 4 x 80 = 320 bytes at FAKE + 16384; d_scales 4 x 4 = 16 bytes at FAKE + 20480;
+    # d_routing_weights at FAKE + 32768
+    a = dict(gate_up=FAKE, io=1, rows=4, inter=40, rw=FAKE + 4096, rwd=0, rw_rows=4, beta=4.0, lb=25.0,
+             go=FAKE + 8192, fmt=0, mode=0, codes=FAKE + 16384, scales=FAKE + 20480, drw=FAKE + 32768, ws=None,
+             wsb=0)
+    a.update(kw)
+    lb = None if a["lb"] is None else ctypes.pointer(ctypes.c_double(a["lb"]))
+    return lib.situ_glu_bwd_mxfp8(a["gate_up"], a["io"], a["rows"], a["inter"], a["rw"], a["rwd"], a["rw_rows"],
+                                  a["beta"], lb, a["go"], a["fmt"], a["mode"], a["codes"], a["scales"], a["drw"],
+                                  a["ws"], a["wsb"], None)
+
+
+BAD_BWD_MX = [
+    dict(io=3), dict(fmt=2), dict(mode=5), dict(beta=-2.0), dict(lb=math.nan), dict(rw_rows=2), dict(go=None),
+    dict(codes=None), dict(scales=None),
+    dict(codes=FAKE + 8192 + 16),                    # overlaps grad_out
+    dict(scales=FAKE + 16384 + 300),                 # overlaps d_codes
+    dict(drw=FAKE + 20480 + 8),                      # overlaps d_scales
+    dict(codes=FAKE + 600),                          # overlaps gate_up
+    dict(rw_rows=1),                                 # broadcast dr needs a workspace
+    dict(rw_rows=1, ws=FAKE + 65536, wsb=8),         # too small (4 rows x 4 bytes)
+    dict(rw_rows=1, ws=FAKE + 20480, wsb=64),        # workspace overlaps d_scales
+    dict(drw=FAKE + 32769),                          # misaligned d_routing_weights
+]
+
+
+@pytest.mark.parametrize("kw", BAD_BWD_MX, ids=[str(k) for k in BAD_BWD_MX])
+def test_bwd_mx_rejects(lib, capi, kw):
+    rc = _bwd_mx(lib, **kw)
+    assert rc == capi.SITU_ERR_INVALID_ARG, (kw, rc)
+    assert capi.last_error(lib) != ""
+
+
+def test_bwd_mx_empty_and_unsupported(lib, capi):
+    assert _bwd_mx(lib, rows=0, rw_rows=0, gate_up=None, go=None, codes=None, scales=None, drw=None) == capi.SITU_OK
+    assert _bwd_mx(lib, inter=0, codes=None, scales=None, drw=None) == capi.SITU_OK
+    assert _bwd_mx(lib, inter=1 << 30, rows=1, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+    assert _bwd_mx(lib, rows=1 << 31, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
 
 
 def _fwd_mx(lib, **kw):
