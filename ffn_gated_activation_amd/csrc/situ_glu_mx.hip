@@ -1,8 +1,8 @@
-// MXFP8 output of the weighted SiTU-GLU forward for CDNA4 (gfx950), and the
-// same block quantiser on its own.
+// MXFP8 output of the weighted SiTU-GLU forward and of its backward's
+// d_gate_up for CDNA4 (gfx950), and the same block quantiser on its own.
 //
 // The Megatron-LM PR "[Dev] Add SiTU-GLU through Transformer Engine" (section
-// "Validation") runs the activation of routed and shared experts under MXFP8
+// "Test results") runs the activation of routed and shared experts under MXFP8
 // block scaling: the activation's output is consumed as MXFP8 by the next
 // projection.  Here the forward writes that form directly, so Y never exists
 // in 16 or 32 bits in HBM.  Format (OCP Microscaling Formats (MX) v1.0 with

@@ -153,7 +153,7 @@ size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate,
 /*
  * Forward with MXFP8 output: Y = r * T_g(G) * T_u(U) as in situ_glu_fwd,
  * written as MXFP8 blocks instead of io_dtype values.  The Megatron-LM PR
- * "[Dev] Add SiTU-GLU through Transformer Engine" (section "Validation") runs
+ * "[Dev] Add SiTU-GLU through Transformer Engine" (section "Test results") runs
  * the activation under MXFP8 block scaling; the format is the OCP
  * Microscaling Formats (MX) v1.0 one:
  *   - each row of Y is cut into blocks of SITU_MX_BLOCK (32) consecutive
@@ -348,7 +348,7 @@ int situ_glu_grouped_fwd(const void *x, int io_dtype, int64_t rows,
  * situ_glu_grouped_fwd on MXFP8 operands: the FC1 GEMM of the routed experts
  * in the MXFP8 block-scaled recipe under which the Megatron-LM PR "[Dev] Add
  * SiTU-GLU through Transformer Engine" validates the activation (sections
- * "Design" and "Validation"), with x and weight held as OCP Microscaling
+ * "Design" and "Test results"), with x and weight held as OCP Microscaling
  * Formats (MX) v1.0 blocks along the contraction axis: 32 consecutive
  * elements of a row share one E8M0 scale byte s, and element k of x row m
  * stands for

@@ -6,7 +6,7 @@
  * header, constant or helper with the GPU library.
  *
  * Where the format comes from.  The Megatron-LM PR "[Dev] Add SiTU-GLU
- * through Transformer Engine" (section "Validation") runs the SiTU-GLU of
+ * through Transformer Engine" (section "Test results") runs the SiTU-GLU of
  * routed and shared experts under MXFP8 block scaling; the pages do not
  * define the format.  Its plain reading is the published OCP definition:
  *   - OCP 8-bit Floating Point Specification (OFP8): element formats
