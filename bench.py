@@ -224,8 +224,9 @@ def _median_ms(fn, n, flush=None) -> float:
 
 def _cold_and_ceilings(kernels: dict, nbytes: dict, rows: int, inter: int, n: int, dev) -> dict:
     """Cold-cache medians of the path's kernels, and plain elementwise kernels
-    of the same byte counts for scale: a copy (1 read : 1 write) and a bf16
-    add (2 : 1, the forward's mix), timed warm (back to back) and cold."""
+    of the same byte counts for scale: a copy (1 read : 1 write), a bf16 add
+    (2 : 1, the forward's mix) and the stream probe at the forward's and the
+    backward's mixes, timed warm (back to back) and cold."""
     import torch
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -242,8 +243,48 @@ def _cold_and_ceilings(kernels: dict, nbytes: dict, rows: int, inter: int, n: in
         cold = _median_ms(fn, n, flush)
         out[name] = {"bytes": nb, "warm_GB/s": round(nb / (warm / 1e3) / 1e9, 2),
                      "cold_GB/s": round(nb / (cold / 1e3) / 1e9, 2)}
+    del b, c
+    out["stream_probe"] = _probe_ceilings(a, n, flush)
     del flush
     return out
+
+
+def _probe_ceilings(a, n: int, flush) -> dict:
+    """The SiTU kernels' access pattern with no arithmetic
+    (libsitu_stream_probe.so, built next to the library): 16-byte
+    non-temporal loads and stores, one wavefront per 4 KiB strip of every
+    stream, at the forward's mix (2 read streams : 1 written) and the
+    backward's (3 : 2, the routing weights aside), streams of the workload's
+    [rows, I] bf16 size.  The memory ceiling of each mix."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "ffn_gated_activation_amd", "libsitu_stream_probe.so")
+    if not os.path.exists(path):
+        return {"error": "libsitu_stream_probe.so is not built (run __graft_entry__.build())"}
+    lib = ctypes.CDLL(path)
+    lib.situ_stream_probe.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+    lib.situ_stream_probe.restype = ctypes.c_int
+    e = a.numel() * a.element_size()
+    ins = [a] + [torch.empty_like(a).normal_() for _ in range(2)]
+    outs = [torch.empty_like(a) for _ in range(2)]
+    res = {"stream_bytes": e}
+    for name, ni, no in (("probe_2to1", 2, 1), ("probe_3to2", 3, 2)):
+        pin = (ctypes.c_void_p * ni)(*[t.data_ptr() for t in ins[:ni]])
+        pout = (ctypes.c_void_p * no)(*[t.data_ptr() for t in outs[:no]])
+
+        def fn():
+            rc = lib.situ_stream_probe(pin, ni, pout, no, e, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"situ_stream_probe returned {rc}")
+        nb = (ni + no) * e
+        warm = _median_ms(fn, n)
+        cold = _median_ms(fn, n, flush)
+        res[name] = {"bytes": nb, "warm_GB/s": round(nb / (warm / 1e3) / 1e9, 2),
+                     "cold_GB/s": round(nb / (cold / 1e3) / 1e9, 2)}
+    del ins, outs
+    return res
 
 
 def _cpu_baseline_grouped(name: str, sample_rows: int) -> dict:

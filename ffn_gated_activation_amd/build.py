@@ -76,5 +76,18 @@ def build_library(verbose: bool = False, extra_hipcc: list[str] | None = None, o
     return out
 
 
+PROBE_LIB = os.path.join(PKG, "libsitu_stream_probe.so")
+
+
+def build_probe(verbose: bool = False, out: str = PROBE_LIB) -> str:
+    """The benchmark's bandwidth probe (csrc/situ_stream_probe.hip), a shared
+    library of its own: not part of libsitu_glu.so or its C ABI."""
+    tmp = out + ".tmp%d" % os.getpid()
+    _run([_hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, os.path.join(CSRC, "situ_stream_probe.hip")], verbose)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-q" not in sys.argv))
+    print(build_probe(verbose="-q" not in sys.argv))

@@ -459,3 +459,28 @@ def test_autograd_rejects_cpu_tensors():
     from ffn_gated_activation_amd import weighted_situ
     with pytest.raises(ValueError):
         weighted_situ(torch.zeros(2, 8, requires_grad=True), torch.ones(2, 1))
+
+
+def test_stream_probe_library_validates_before_launch():
+    """The benchmark's bandwidth probe (its own library, outside the C ABI
+    above): exported, and every malformed call is rejected with 1 before
+    any launch; a zero-byte call launches nothing."""
+    from ffn_gated_activation_amd.build import PROBE_LIB, build_probe
+    if not os.path.exists(PROBE_LIB):
+        build_probe()
+    p = ctypes.CDLL(PROBE_LIB)
+    f = p.situ_stream_probe
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    fake = 1 << 20
+    ins = (ctypes.c_void_p * 4)(fake, fake + 4096, fake + 8192, fake + 12288)
+    outs = (ctypes.c_void_p * 2)(fake + 16384, fake + 20480)
+    assert f(ins, 2, outs, 1, 0, None) == 0
+    for n_in, n_out, nbytes in ((0, 1, 16), (5, 1, 16), (2, 0, 16), (2, 3, 16), (2, 1, 8), (2, 1, -16),
+                                (2, 1, (1 << 40) + 16)):
+        assert f(ins, n_in, outs, n_out, nbytes, None) == 1, (n_in, n_out, nbytes)
+    bad = (ctypes.c_void_p * 2)(fake + 8, fake)
+    assert f(bad, 2, outs, 1, 16, None) == 1
+    assert f(ins, 2, (ctypes.c_void_p * 1)(0), 1, 16, None) == 1
+    assert f(None, 2, outs, 1, 16, None) == 1
