@@ -183,12 +183,13 @@ template <bool LB, bool FAST, bool PRECISE>
 __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const GateK &gk, const UpK &uk)
 {
     const Gate t = gate_parts<FAST, PRECISE>(g, rscale, gk);
-    const float m = (1.0f + t.e2) + fmaf(t.e1, t.e2, t.e1);  // (1 + e1)(1 + e2)
+    const float a = 1.0f + t.e1;
+    const float m = fmaf(t.e2, a, a);  // (1 + e1)(1 + e2)
     if (LB) {
         const float z = fabsf(u) * uk.ku;  // v = 2^-z = exp(-2|U|/b2)
         const float v = ex2(-z);
         const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 1>(z, v, 1.0f), u);
-        const float q = rcp(m * (1.0f + v));
+        const float q = rcp(fmaf(m, v, m));  // 1 / ((1 + e1)(1 + e2)(1 + v))
         return (t.nt * t.sn_s) * (nu * q);
     } else {
         const float q = rcp(m);
