@@ -477,8 +477,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the weighted SiTU-GLU path is row parallel and this build "
-              "runs on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        print("bench.py measures one GPU: the weighted SiTU-GLU path is row parallel and is measured "
+              "on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
         return 2
 
     import torch
