@@ -99,6 +99,11 @@ constexpr int kXcdRows = 8;            // row tiles of an XCD's block in the XCD
 constexpr int kFirstLoads = 8;         // of a stage's 16 loads per thread: issued at the boundary, the rest
                                        // during the next k step
 constexpr int kLoadSpacing = 2;        // products between consecutive loads
+// fp8 operands (two k steps per stage, each product twice the work): 12 of
+// the loads at the boundary, one per product (measured 5% faster than 8 / 2;
+// bf16 is fastest with 8 / 2)
+constexpr int kFirstLoadsF8 = 12;
+constexpr int kLoadSpacingF8 = 1;
 
 using lds_ptr_t = __attribute__((address_space(3))) void *;
 
@@ -392,7 +397,7 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
     using Buf1 = std::integral_constant<int, 1>;
     Frags f0, f1;
     Scales q0, q1;  // scales of the stage in buffer 0 / buffer 1 (fp8)
-    constexpr int kFirst = kFirstLoads, kSpread = kLoadSpacing;
+    constexpr int kFirst = F8 ? kFirstLoadsF8 : kFirstLoads, kSpread = F8 ? kLoadSpacingF8 : kLoadSpacing;
     // k steps 0..kSteps-2 of a stage: products of step st, fragments of step
     // st + 1 (and the remaining loads of stage kt_next into the other buffer)
     auto first_steps = [&](auto buf, int kt_next) {
