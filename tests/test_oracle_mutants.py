@@ -128,6 +128,19 @@ MXDQ_MUTANTS = {
 }
 
 
+GROUPED_MX_MUTANTS = {
+    "mxg_weight_scales_of_expert_0": (
+        "np.asarray(w_scales, dtype=np.uint8).reshape(E * two_i, -1)",
+        "np.ascontiguousarray(np.broadcast_to(np.asarray(w_scales, dtype=np.uint8)[:1], "
+        "np.asarray(w_scales).shape)).reshape(E * two_i, -1)"),
+    "mxg_x_scales_rows_reversed": ("x = mx_dequantize(xc, x_scales, fmt, lib=lib)",
+                                   "x = mx_dequantize(xc, np.asarray(x_scales)[::-1], fmt, lib=lib)"),
+    "mxg_weight_format_swapped": (".reshape(E * two_i, -1), fmt,",
+                                  ".reshape(E * two_i, -1), 'e5m2' if fmt == 'e4m3' else 'e4m3',"),
+    "mxg_weight_rows_transposed": ("wc.reshape(E * two_i, K)", "wc.transpose(1, 0, 2).reshape(E * two_i, K)"),
+}
+
+
 def _py_mutant(func, table, name):
     import inspect
     old, new = table[name]
@@ -198,3 +211,19 @@ def test_mutant_is_caught(name):
             except (AssertionError, ValueError, FloatingPointError, OverflowError) as e:
                 caught.append(pin.__name__)
         assert caught, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED_MX_MUTANTS))
+def test_grouped_mx_mutant_is_caught(name, monkeypatch):
+    """Mistakes in how the block-scaled grouped oracle decodes its operands
+    (the composition of mx_dequantize and grouped_glu_forward)."""
+    monkeypatch.setattr(oracle, "grouped_glu_forward_mx",
+                        _py_mutant(oracle.grouped_glu_forward_mx, GROUPED_MX_MUTANTS, name))
+    lib = oracle.load()
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
