@@ -28,14 +28,14 @@ SITU_MX_BLOCK = 32
 SITU_GROUPED_MAX_EXPERTS = 4096
 SITU_GROUPED_MAX_HIDDEN = 1 << 20
 SITU_GROUPED_MAX_INTERMEDIATE = 1 << 20
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # every symbol include/situ_glu.h declares
 EXPORTED = ("situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes",
             "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window",
             "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize", "situ_glu_attn_res_fwd",
             "situ_glu_grouped_fwd", "situ_glu_grouped_fwd_mxfp8",
-            "situ_glu_grouped_fwd_mxfp8_workspace_bytes", "situ_glu_bwd_mxfp8")
+            "situ_glu_grouped_fwd_mxfp8_workspace_bytes", "situ_glu_bwd_mxfp8", "situ_glu_split")
 
 
 class SituGluError(RuntimeError):
@@ -63,6 +63,8 @@ def _bind(lib):
     lib.situ_glu_abi_version.argtypes = []
     lib.situ_glu_gate_window.restype = i32
     lib.situ_glu_gate_window.argtypes = [dbl, ctypes.POINTER(ctypes.c_float)]
+    lib.situ_glu_split.restype = i32
+    lib.situ_glu_split.argtypes = [i32, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int64)]
     lib.situ_glu_fwd_mxfp8.restype = i32
     lib.situ_glu_fwd_mxfp8.argtypes = [vp, i32, i64, i64, vp, i32, i64, dbl, dblp, i32, i32, vp, vp, vp]
     lib.situ_glu_bwd_mxfp8.restype = i32

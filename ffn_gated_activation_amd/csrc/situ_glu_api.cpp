@@ -187,6 +187,24 @@ Jet gate_grad_series(long double b1, long double x0)
     return jdiv(jmul(e2, br), den);
 }
 
+// dT_g/dG at G < 0 in long double, from the same closed form.
+long double gate_grad_at(long double b1, long double x)
+{
+    const long double e1 = expl(2.0L * x / b1), e2 = expl(x);
+    const long double A = 1.0L + e1, B = 1.0L + e2;
+    return e2 * (4.0L * e1 * B - b1 * (1.0L - e1 * e1)) / (A * A * B * B);
+}
+
+// Round a finite float to the nearest bf16 value (ties to even).
+float round_to_bf16(float f)
+{
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
 // The bracket 4 e1 (1 + e2) - b1 (1 - e1^2) as a function of a = -G > 0:
 // positive at a = 0 (value 8), tends to -b1; its zero is -G*.
 long double bracket_at(long double b1, long double a)
@@ -235,13 +253,9 @@ GateK make_gate_consts(double beta1)
     if (fabsl(gstar) / 4.0L < hw)
         hw = fabsl(gstar) / 4.0L;
     k.win_hw = (float)hw;
-    // The quadratic (bf16 io, 1 ulp = 2^-8 relative) drops c3 d^3: keep
-    // |c3/c1| hw2^2 <= 1e-4, inside the cubic's window.
-    long double hw2 = hw;
-    const long double q2 = fabsl(s.c[3]) > 0 ? sqrtl(1e-4L * fabsl(s.c[1] / s.c[3])) : hw;
-    if (q2 < hw2)
-        hw2 = q2;
-    k.win_hw2 = (float)hw2;
+    // bf16 io: the bf16 value nearest G* and its exact dT_g/dG / 4
+    k.gsub = round_to_bf16(ghi);
+    k.tsub = (float)(gate_grad_at(b1, (long double)k.gsub) / 4.0L);
     return k;
 }
 
@@ -268,6 +282,75 @@ int rows_per_block_override()
         return (x >= 1 && x <= 16) ? x : 0;
     }();
     return v;
+}
+
+int env_override(const char *name, int lo, int hi)
+{
+    const char *e = std::getenv(name);
+    const int x = e ? std::atoi(e) : 0;
+    return (x >= lo && x <= hi) ? x : 0;
+}
+
+// Work split of the 128-bit path (chunks of 1 KiB of every stream; see
+// situ::ChunkGeom).  Measured on MI355X with bf16 io: single-wavefront
+// workgroups of one chunk each read and write at 6.5-6.8 TB/s, the copy
+// ceiling of that pattern; with a linear beta the up branch's arithmetic
+// needs two chunks per wavefront (the second one's loads in flight during the
+// first one's math), and the backward four wavefronts per workgroup.  Longer
+// chunk runs per wavefront and persistent grid-stride loops were slower.
+// SITU_GLU_CHUNKS_PER_WAVE (1..8) and SITU_GLU_WAVES_PER_BLOCK (1..4) override
+// the choice (tuning).
+constexpr int kDrWavesPerBlock = 4;  // row mapping: target wavefronts per workgroup
+constexpr int kMaxRowWaves = 16;     // row mapping: wavefronts per row at most
+
+int plan_split(int64_t rows, int64_t inter, int64_t es, bool bwd, bool lb, bool row_dr, situ::ChunkSplit &sp)
+{
+    static const int env_k = env_override("SITU_GLU_CHUNKS_PER_WAVE", 1, 8);
+    static const int env_w = env_override("SITU_GLU_WAVES_PER_BLOCK", 1, 4);
+    situ::ChunkGeom g{};
+    const int64_t half = inter * es;
+    const int64_t cpr = (half + 1023) / 1024;
+    const int64_t total = rows * cpr;
+    if (total >= ((int64_t)1 << 31))
+        return fail(SITU_ERR_UNSUPPORTED, "%lld rows of %lld bytes each exceed 2^31 KiB per half",
+                    (long long)rows, (long long)half);
+    g.half = (uint32_t)half;
+    g.cpr = (int)cpr;
+    if (cpr > 1) {
+        // chunk / cpr = floor(chunk * magic / 2^(31 + l)) for every chunk < 2^31
+        int l = 0;
+        while (((int64_t)1 << l) < cpr)
+            ++l;
+        g.magic = (uint32_t)((((uint64_t)1) << (31 + l)) / (uint64_t)cpr + 1);
+        g.shift = l - 1;
+    }
+    int k = es == 2 ? (lb ? 2 : 1) : 2;
+    int wpb = es == 2 && bwd && lb ? 4 : 1;
+    if (env_k)
+        k = env_k;
+    if (env_w)
+        wpb = env_w;
+    if (!row_dr) {
+        const int64_t waves = (total + k - 1) / k;
+        g.k = k;
+        sp.grid = (unsigned)((waves + wpb - 1) / wpb);
+        sp.block = 64 * wpb;
+    } else {
+        const int64_t kmin = (cpr + kMaxRowWaves - 1) / kMaxRowWaves;
+        const int64_t kr = k < kmin ? kmin : k;
+        const int wpr = (int)((cpr + kr - 1) / kr);
+        int rpb = (env_w ? env_w : kDrWavesPerBlock) / wpr;
+        if (rpb < 1)
+            rpb = 1;
+        g.k = (int)kr;
+        g.wpr = wpr;
+        g.wmagic = (uint32_t)((256 + wpr - 1) / wpr);
+        sp.grid = (unsigned)((rows + rpb - 1) / rpb);
+        sp.block = 64 * wpr * rpb;
+    }
+    sp.geom = g;
+    sp.total = (uint32_t)total;
+    return SITU_OK;
 }
 
 // The constants depend on beta alone; keep the last one per thread.
@@ -303,7 +386,7 @@ size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate, int64_t 
 
 // Exposed for tests: the root-window constants the kernels use for a beta:
 // out[0] = G*_f32, out[1] = cubic half width, out[2..5] = c0..c3,
-// out[6] = quadratic half width.
+// out[6] = the bf16 value nearest G*, out[7] = dT_g/dG there.
 int situ_glu_gate_window(double beta, float *out)
 {
     g_last_error.clear();
@@ -318,7 +401,41 @@ int situ_glu_gate_window(double beta, float *out)
     out[3] = k.c1;
     out[4] = k.c2;
     out[5] = k.c3;
-    out[6] = k.win_hw2;
+    out[6] = k.gsub;
+    out[7] = 4.0f * k.tsub;
+    return SITU_OK;
+}
+
+int situ_glu_split(int io_dtype, int64_t rows, int64_t intermediate, int linear_beta_given, int direction,
+                   int64_t *out)
+{
+    g_last_error.clear();
+    if (!dtype_ok(io_dtype))
+        return fail(SITU_ERR_INVALID_ARG, "io_dtype %d is not SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1)", io_dtype);
+    if (direction < 0 || direction > 2)
+        return fail(SITU_ERR_INVALID_ARG, "direction %d is not 0, 1 or 2", direction);
+    if (!out)
+        return fail(SITU_ERR_INVALID_ARG, "out is NULL");
+    if (rows < 1 || rows > (int64_t)0x7fffffff || intermediate < 1 || intermediate > (int64_t)0x3fffffff)
+        return fail(SITU_ERR_INVALID_ARG, "sizes out of range (rows=%lld, intermediate=%lld)", (long long)rows,
+                    (long long)intermediate);
+    const int64_t es = dtype_bytes(io_dtype);
+    if ((intermediate * es) % 16 || intermediate * 2 * es >= ((int64_t)1 << 31))
+        return fail(SITU_ERR_INVALID_ARG, "these sizes take the element path (no chunk split)");
+    situ::ChunkSplit sp{};
+    const int rc = plan_split(rows, intermediate, es, direction > 0, linear_beta_given != 0, direction == 2, sp);
+    if (rc)
+        return rc;
+    out[0] = sp.geom.cpr;
+    out[1] = sp.total;
+    out[2] = sp.geom.k;
+    out[3] = sp.geom.wpr;
+    out[4] = sp.grid;
+    out[5] = sp.block;
+    out[6] = sp.geom.magic;
+    out[7] = sp.geom.shift;
+    out[8] = sp.geom.wmagic;
+    out[9] = sp.geom.half;
     return SITU_OK;
 }
 
@@ -357,7 +474,8 @@ int situ_glu_fwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
             intermediate * 2 * es < ((int64_t)1 << 31);
     L.lb = linear_beta != nullptr;
     L.fast = beta == 4.0;
-    L.rows_per_block = rows_per_block_override();
+    if (L.vec && (rc = plan_split(rows, intermediate, es, false, L.lb, false, L.split)))
+        return rc;
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
     const int err = situ::launch_fwd(L, stream);
@@ -438,7 +556,8 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
             (intermediate * es) % 16 == 0 && intermediate * 2 * es < ((int64_t)1 << 31);
     L.lb = linear_beta != nullptr;
     L.fast = beta == 4.0;
-    L.rows_per_block = rows_per_block_override();
+    if (L.vec && (rc = plan_split(rows, intermediate, es, true, L.lb, d_routing_weights != nullptr, L.split)))
+        return rc;
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
     const int err = situ::launch_bwd(L, stream);

@@ -197,18 +197,19 @@ __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const 
     }
 }
 
-// dT_g/dG / 4 near its root: polynomial in d = G - G*_f32 inside the window
-// (cubic for fp32 io, quadratic for bf16 io); `plain` elsewhere.
+// dT_g/dG / 4 near its root, where its two terms cancel.  fp32 io: the
+// cubic in d = G - G*_f32 inside the window.  bf16 io: G is a bf16 value, and
+// only the one nearest the root loses more than ~3e-5 to the cancellation;
+// that value gets its exact dT_g/dG / 4.  `plain` elsewhere.
 template <bool PRECISE>
 __device__ __forceinline__ float gate_grad4_window(float g, float plain, const GateK &k)
 {
-    const float d = g - k.win_ghi;  // exact (Sterbenz) inside the window
     if (PRECISE) {
+        const float d = g - k.win_ghi;  // exact (Sterbenz) inside the window
         const float p = fmaf(fmaf(fmaf(0.25f * k.c3, d, 0.25f * k.c2), d, 0.25f * k.c1), d, 0.25f * k.c0);
         return fabsf(d) <= k.win_hw ? p : plain;
     } else {
-        const float p = fmaf(fmaf(0.25f * k.c2, d, 0.25f * k.c1), d, 0.25f * k.c0);
-        return fabsf(d) <= k.win_hw2 ? p : plain;
+        return g == k.gsub ? k.tsub : plain;
     }
 }
 
@@ -222,12 +223,14 @@ struct BwdOut {
 // and since q m C = 1:
 //   go T_g T_u / (b1 b2) = X a1 nu,  dU = X a1 v (q m) cU,
 //   dG = go nu (q m) (T_g' / 4) cG,  T_g' / 4 = |sn| br (q C)^2.
-template <bool LB, bool FAST, bool PRECISE>
+// FOLD (no routing-weight gradient, so p is not needed): cU rides on nt and
+// cG on nu (linear beta), one multiply fewer per gradient.
+template <bool LB, bool FAST, bool PRECISE, bool FOLD = false>
 __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG, float cU,
                                            const GateK &gk, const UpK &uk)
 {
     BwdOut o;
-    const Gate t = gate_parts<FAST, PRECISE>(g, 1.0f, gk);
+    const Gate t = gate_parts<FAST, PRECISE>(g, FOLD ? cU : 1.0f, gk);
     // T_g' / (4 sn) * (A B)^2 = e1 B + (b1/4) sgn(G) (1 - e1^2) snc, e1 B = e1 + e1 e2
     const float om = FAST ? 1.0f - t.e2 : (0.25f * gk.beta1) * fmaf(-t.e1, t.e1, 1.0f);
     const float e1B = fmaf(t.e1, t.e2, t.e1);
@@ -240,7 +243,7 @@ __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG,
         const float z = fabsf(u) * (0.5f * uk.ku);
         const float h = ex2(-z);
         const float v = h * h;
-        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 2>(z, v, 1.0f), u);
+        const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 2>(z, v, FOLD ? cG : 1.0f), u);
         const float C = 1.0f + v;
         const float q = rcp(m * C);
         const float iab = q * C;                 // 1 / (A B)
@@ -248,14 +251,14 @@ __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG,
         const float tgp = gate_grad4_window<PRECISE>(g, sbr * (iab * iab), gk);  // T_g' / 4
         const float xa1 = (go * q) * a1;
         o.p = xa1 * nu;
-        o.du = xa1 * v * ic * cU;
-        o.dg = go * nu * ic * tgp * cG;
+        o.du = FOLD ? xa1 * v * ic : xa1 * v * ic * cU;
+        o.dg = FOLD ? go * nu * ic * tgp : go * nu * ic * tgp * cG;
     } else {
         const float q = rcp(m);
         const float tgp = gate_grad4_window<PRECISE>(g, sbr * (q * q), gk);
         const float z1 = go * (a1 * q);          // go T_g / b1
         o.p = z1 * u;
-        o.du = z1 * cU;
+        o.du = FOLD ? z1 : z1 * cU;
         o.dg = go * u * tgp * cG;
     }
     return o;

@@ -14,15 +14,18 @@ namespace situ {
 // Inside |G - win_ghi| <= win_hw the fp32-io kernels evaluate dT_g/dG as the
 // cubic c0 + c1 d + c2 d^2 + c3 d^3 in d = G - win_ghi (the Taylor expansion
 // at the fp32 number nearest G*) instead of the cancelling difference; the
-// bf16-io kernels use the quadratic c0 + c1 d + c2 d^2 inside win_hw2.
+// bf16-io kernels, whose inputs are bf16 values, replace dT_g/dG / 4 at the
+// one bf16 value nearest G* (gsub) by its exact value (tsub); at every
+// other bf16 value the plain formula loses at most a factor ~250 to the
+// cancellation (about 3e-5 relative), far inside a bf16 ulp.
 struct GateK {
     float beta1;
     float k1;
     float y1k;
     float win_ghi;
     float win_hw;
-    float win_hw2;
     float c0, c1, c2, c3;
+    float gsub, tsub;
 };
 
 // Up-branch constant (only used when linear_beta is given):
@@ -33,6 +36,33 @@ struct UpK {
 };
 
 enum { IO_F32 = 0, IO_BF16 = 1 };
+
+// Work split of the 128-bit path.  A chunk is 64 lanes x one 16-byte vector
+// of every stream: 1 KiB of each half row.  A wavefront takes `k`
+// consecutive chunks (loads of the next issued before the math of the
+// current one).  Flat mapping: chunks numbered row-major over the whole
+// tensor, wavefront w takes chunks w k .. w k + k - 1, `wpb` wavefronts per
+// workgroup.  Row mapping (routing-weight gradient): a row's chunks go to
+// `wpr` wavefronts of one workgroup, `rpb` rows per workgroup, and the
+// row's partial sums meet in LDS.
+struct ChunkGeom {
+    uint32_t half;        // bytes of a half row (= bytes of an output row)
+    int cpr;              // chunks per row
+    uint32_t magic;       // chunk index / cpr = mulhi(index, magic) >> shift (cpr > 1)
+    int shift;
+    int k;                // chunks per wavefront
+    int wpr;              // row mapping: wavefronts per row
+    uint32_t wmagic;      // row mapping: slot / wpr = (slot * wmagic) >> 8 for slot < 16
+};
+
+// A launch of the 128-bit path: geometry, chunks of the tensor (flat
+// mapping), workgroups and threads per workgroup.
+struct ChunkSplit {
+    ChunkGeom geom;
+    uint32_t total;
+    unsigned grid;
+    int block;
+};
 
 struct FwdLaunch {
     const void *gate_up;
@@ -46,7 +76,7 @@ struct FwdLaunch {
     int vec;              // 1: 128-bit path, 0: element path
     int lb;               // linear_beta given
     int fast;             // beta1 == 4 specialisation
-    int rows_per_block;   // 128-bit path, rows of one strip: rows per workgroup (0 = default)
+    ChunkSplit split;     // 128-bit path
     GateK gk;
     UpK uk;
 };
@@ -66,7 +96,7 @@ struct BwdLaunch {
     int vec;
     int lb;
     int fast;
-    int rows_per_block;   // 128-bit path, rows of one strip: rows per workgroup (0 = default)
+    ChunkSplit split;     // 128-bit path (row mapping when d_rw)
     GateK gk;
     UpK uk;
 };

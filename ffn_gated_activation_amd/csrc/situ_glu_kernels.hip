@@ -9,18 +9,22 @@
 // per-row reduction dr = sum_j go T_g T_u.
 //
 // Memory-bound elementwise work, no contraction, so no MFMA.  Layout of the
-// work: one workgroup per group of rows; a row is cut into strips of
-// 64 lanes x kUnroll 128-bit vectors of each half row, and each wavefront
-// owns one strip at a time (long rows get several wavefronts, whose dr
-// partials meet in LDS).  Loads and stores go through buffer descriptors
-// with the non-temporal hint.
+// work (128-bit path): a row is cut into chunks of 64 lanes x one 16-byte
+// vector of each stream (1 KiB of each half row); a wavefront takes k
+// consecutive chunks, issuing the next chunk's loads before the current
+// chunk's math, and ends.  Without a routing-weight gradient the chunks are
+// numbered over the whole tensor (flat mapping, one-wavefront workgroups by
+// default); with it a row's chunks go to the wavefronts of one workgroup,
+// whose partial sums meet in LDS.  Loads and stores go through buffer
+// descriptors with the non-temporal hint.
 //
 // The per-element math (one reciprocal per element, Taylor replacements where
 // a difference cancels) is in situ_glu_device.h.
 // For b1 = 4, e1 = exp(-a/2) and e2 = e1^2: one exponential for the gate.
 // nt = 1 - exp(-y) cancels for small y; there its Taylor series is used.
-// T_g' cancels near its root G* < 0; there a polynomial in G - G* (built on
-// the host for the given b1) replaces it.
+// T_g' cancels near its root G* < 0; there a polynomial in G - G* (fp32 io)
+// or the exact value at the one bf16 input nearest G* (bf16 io), both built
+// on the host for the given b1, replace it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,150 +34,275 @@
 namespace situ {
 namespace {
 
-// 128-bit vectors in flight per lane and input stream; a wavefront's strip
-// is 64 lanes x unroll vectors of each half row.  Measured on MI355X: 4 for
-// the forward (2 input streams) and 2 for the backward (3 input streams,
-// which then fits in 64 VGPRs: 8 wavefronts per SIMD).
-#ifndef SITU_UNROLL_FWD
-#define SITU_UNROLL_FWD 4
-#endif
-#ifndef SITU_UNROLL_BWD
-#define SITU_UNROLL_BWD 2
-#endif
-constexpr int kUnrollFwd = SITU_UNROLL_FWD;
-constexpr int kUnrollBwd = SITU_UNROLL_BWD;
-#ifndef SITU_BWD_MIN_WAVES
-#define SITU_BWD_MIN_WAVES 8  // wavefronts per SIMD the backward must fit (<= 64 VGPRs)
-#endif
+constexpr uint32_t kChunkBytes = 1024;  // 64 lanes x 16 bytes of each stream
 
-template <int IO, bool LB, bool FAST>
-__global__ void __launch_bounds__(64 * kMaxWaves)
-situ_glu_fwd_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
-                        int64_t rw_stride, void *__restrict__ out, int64_t rows, int inter, int waves_per_row,
-                        GateK gk, UpK uk)
+// One chunk's streams: buffer descriptors (range = the chunk, or empty for a
+// chunk past the wavefront's share: loads return zeros, stores are dropped)
+// and the bits of the row's routing weight (fp32, or bf16 in the low half),
+// converted only by the chunk's math.  The weight's dtype is a template
+// parameter (RWB: bf16), so that no chunk's loads wait behind a branch on it
+// or behind the weight's own load.
+template <int NIN, int NOUT>
+struct Chunk {
+    rsrc_t in[NIN];
+    rsrc_t out[NOUT];
+    uint32_t rbits;
+};
+
+template <bool RWB>
+__device__ __forceinline__ float weight_of(uint32_t rbits)
 {
-    constexpr bool PRECISE = IO == IO_F32;
-    using T = Io<IO>;
-    constexpr int E = T::kPerVec;
-    constexpr int kUnroll = kUnrollFwd, kStrip = 64 * kUnroll;
-    const int lane = threadIdx.x & 63;
-    const Place pl = place(waves_per_row);
-    if (pl.row >= rows)
-        return;
-    const int nv = inter / E;
-    const uint32_t half = (uint32_t)nv * 16u;  // bytes of a half row = an output row
-    const int spr = (nv + kStrip - 1) / kStrip;
-    const char *row = static_cast<const char *>(gate_up) + pl.row * (int64_t)half * 2;
-    const rsrc_t rg = make_rsrc(row, half), ru = make_rsrc(row + half, half);
-    const rsrc_t ro = make_rsrc(static_cast<char *>(out) + pl.row * (int64_t)half, half);
-    const float r = load_rw(rw, rw_bf16, pl.row * rw_stride);
-    const float rscale = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
-    for (int s = pl.strip0; s < spr; s += pl.wpr) {
-        uint4 gv[kUnroll], uv[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
-            gv[k] = bload(rg, off);
-            uv[k] = bload(ru, off);
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            // past the row end the loads returned zeros and the store is dropped
-            const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
-            float g[E], u[E], y[E];
-            T::unpack(gv[k], g);
-            T::unpack(uv[k], u);
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                y[e] = fwd_elem<LB, FAST, PRECISE>(g[e], u[e], rscale, gk, uk);
-            bstore(ro, off, T::pack(y));
-        }
-    }
+    return __uint_as_float(RWB ? rbits << 16 : rbits);
 }
 
-template <int IO, bool LB, bool FAST, bool DR>
-__global__ void __launch_bounds__(64 * kMaxWaves, SITU_BWD_MIN_WAVES)
-situ_glu_bwd_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
-                        int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
-                        void *__restrict__ d_rw, float *__restrict__ row_partials, int64_t rows, int inter,
-                        int waves_per_row, GateK gk, UpK uk)
+// Streams of chunk c of a row.  NIN = 2: gate_up halves; 3: plus grad_out.
+// NOUT = 1: out [rows, I]; 2: d_gate_up halves.
+template <bool RWB>
+__device__ __forceinline__ uint32_t weight_bits(const void *rw, int64_t i)
 {
-    constexpr bool PRECISE = IO == IO_F32;
+    return RWB ? (uint32_t)static_cast<const uint16_t *>(rw)[i] : static_cast<const uint32_t *>(rw)[i];
+}
+
+template <int NIN, int NOUT>
+__device__ __forceinline__ Chunk<NIN, NOUT> chunk_at(int64_t row, uint32_t c, bool live, const ChunkGeom &g,
+                                                      const char *gu, const char *go, char *o, uint32_t rbits)
+{
+    Chunk<NIN, NOUT> k;
+    const uint32_t off = c * kChunkBytes;
+    const uint32_t left = g.half - off;
+    const uint32_t n = live ? (left < kChunkBytes ? left : kChunkBytes) : 0u;
+    row = live ? row : 0;
+    const char *gr = gu + row * (int64_t)g.half * 2 + off;
+    k.in[0] = make_rsrc(gr, n);
+    k.in[1] = make_rsrc(gr + g.half, n);
+    if constexpr (NIN == 3)
+        k.in[2] = make_rsrc(go + row * (int64_t)g.half + off, n);
+    if constexpr (NOUT == 1) {
+        k.out[0] = make_rsrc(o + row * (int64_t)g.half + off, n);
+    } else {
+        char *orow = o + row * (int64_t)g.half * 2 + off;
+        k.out[0] = make_rsrc(orow, n);
+        k.out[1] = make_rsrc(orow + g.half, n);
+    }
+    k.rbits = rbits;
+    return k;
+}
+
+// Issue one chunk's loads.  The scheduling fences keep each chunk's loads
+// ahead of the previous chunk's math, as written.
+template <int NIN, int NOUT>
+__device__ __forceinline__ void load_chunk(uint4 *v, const Chunk<NIN, NOUT> &k, uint32_t voff)
+{
+#pragma unroll
+    for (int i = 0; i < NIN; ++i)
+        v[i] = bload(k.in[i], voff);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int IO, bool LB, bool FAST, bool RWB>
+__device__ __forceinline__ void fwd_chunk(const uint4 *v, const Chunk<2, 1> &k, uint32_t voff, const GateK &gk,
+                                          const UpK &uk)
+{
     using T = Io<IO>;
     constexpr int E = T::kPerVec;
-    constexpr int kUnroll = kUnrollBwd, kStrip = 64 * kUnroll;
-    __shared__ float wave_part[kMaxWaves];
-    const int lane = threadIdx.x & 63;
-    const Place pl = place(waves_per_row);
-    const bool live = pl.row < rows;
-    float acc = 0.0f;
-    if (live) {
-        const int nv = inter / E;
-        const uint32_t half = (uint32_t)nv * 16u;
-        const int spr = (nv + kStrip - 1) / kStrip;
-        const char *row = static_cast<const char *>(gate_up) + pl.row * (int64_t)half * 2;
-        const rsrc_t rg = make_rsrc(row, half), ru = make_rsrc(row + half, half);
-        const rsrc_t rgo = make_rsrc(static_cast<const char *>(grad_out) + pl.row * (int64_t)half, half);
-        char *drow = static_cast<char *>(d_gate_up) + pl.row * (int64_t)half * 2;
-        const rsrc_t rdg = make_rsrc(drow, half), rdu = make_rsrc(drow + half, half);
-        const float r = load_rw(rw, rw_bf16, pl.row * rw_stride);
-        const float cG = LB ? 4.0f * r * uk.beta2 : 4.0f * r;
-        const float cU = LB ? 4.0f * r * gk.beta1 : r * gk.beta1;
-        for (int s = pl.strip0; s < spr; s += pl.wpr) {
-            uint4 gv[kUnroll], uv[kUnroll], ov[kUnroll];
+    const float r = weight_of<RWB>(k.rbits);
+    const float rscale = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
+    float g[E], u[E], y[E];
+    T::unpack(v[0], g);
+    T::unpack(v[1], u);
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
-                gv[k] = bload(rg, off);
-                uv[k] = bload(ru, off);
-                ov[k] = bload(rgo, off);
-            }
-    #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                // past the row end all three loads returned zeros: every term
-                // below is then an exact zero and the stores are dropped
-                const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
-                float g[E], u[E], og[E], dg[E], du[E];
-                T::unpack(gv[k], g);
-                T::unpack(uv[k], u);
-                T::unpack(ov[k], og);
+    for (int e = 0; e < E; ++e)
+        y[e] = fwd_elem<LB, FAST, IO == IO_F32>(g[e], u[e], rscale, gk, uk);
+    bstore(k.out[0], voff, T::pack(y));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// DR: accumulate go T_g T_u / (b1 b2) (/ b1 without linear beta) into acc;
+// otherwise the row scales ride on the gradients' factors (FOLD).
+template <int IO, bool LB, bool FAST, bool RWB, bool DR>
+__device__ __forceinline__ void bwd_chunk(const uint4 *v, const Chunk<3, 2> &k, uint32_t voff, const GateK &gk,
+                                          const UpK &uk, float &acc)
+{
+    using T = Io<IO>;
+    constexpr int E = T::kPerVec;
+    const float r = weight_of<RWB>(k.rbits);
+    const float cG = LB ? 4.0f * r * uk.beta2 : 4.0f * r;
+    const float cU = LB ? 4.0f * r * gk.beta1 : r * gk.beta1;
+    float g[E], u[E], og[E], dg[E], du[E];
+    T::unpack(v[0], g);
+    T::unpack(v[1], u);
+    T::unpack(v[2], og);
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const BwdOut b = bwd_elem<LB, FAST, PRECISE>(g[e], u[e], og[e], cG, cU, gk, uk);
-                    dg[e] = b.dg;
-                    du[e] = b.du;
-                    if (DR)
-                        acc += b.p;
-                }
-                bstore(rdg, off, T::pack(dg));
-                bstore(rdu, off, T::pack(du));
-            }
-        }
+    for (int e = 0; e < E; ++e) {
+        const BwdOut b = bwd_elem<LB, FAST, IO == IO_F32, !DR>(g[e], u[e], og[e], cG, cU, gk, uk);
+        dg[e] = b.dg;
+        du[e] = b.du;
+        if (DR)
+            acc += b.p;
     }
-    if (DR) {
-        const float scale = LB ? gk.beta1 * uk.beta2 : gk.beta1;
-        const float s = wave_sum(acc);
-        if (pl.wpr == 1) {
-            if (live && lane == 0)
-                write_row_dr(s * scale, pl.row, rw_stride, rw_bf16, d_rw, row_partials);
-        } else {
-            // the row's wavefronts meet in LDS; the first one adds them in order
-            if (lane == 0)
-                wave_part[pl.slot] = s;
-            __syncthreads();
-            if (live && pl.strip0 == 0 && lane == 0) {
-                float t = 0.0f;
-                for (int w = 0; w < pl.wpr; ++w)
-                    t += wave_part[pl.slot + w];
-                write_row_dr(t * scale, pl.row, rw_stride, rw_bf16, d_rw, row_partials);
-            }
+    bstore(k.out[0], voff, T::pack(dg));
+    bstore(k.out[1], voff, T::pack(du));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// chunk index -> (row, chunk in row)
+__device__ __forceinline__ void locate(uint32_t u, const ChunkGeom &g, int64_t &row, uint32_t &c)
+{
+    const uint32_t q = g.cpr == 1 ? u : __umulhi(u, g.magic) >> g.shift;
+    row = q;
+    c = u - q * (uint32_t)g.cpr;
+}
+
+// The wavefront's n chunks (n >= 1), two register sets: the loads of chunk
+// i + 1 are in flight during chunk i's math.  `step(row, c)` moves to the
+// next chunk.  WEIGHT(row) gives the row's weight bits; BODY(regs, chunk) is
+// the math and the stores.
+#define SITU_CHUNK_PIPELINE(NIN, NOUT, WEIGHT, BODY)                                                       \
+    {                                                                                             \
+        uint4 A[NIN], B[NIN];                                                                     \
+        Chunk<NIN, NOUT> ka = chunk_at<NIN, NOUT>(row, c, true, g, gp, gop, op, WEIGHT(row)); \
+        load_chunk(A, ka, voff);                                                                  \
+        step(row, c);                                                                             \
+        Chunk<NIN, NOUT> kb = chunk_at<NIN, NOUT>(row, c, 1 < n, g, gp, gop, op, WEIGHT(row)); \
+        load_chunk(B, kb, voff);                                                                  \
+        BODY(A, ka);                                                                              \
+        int i = 1;                                                                                \
+        for (; i + 2 <= n; i += 2) {                                                              \
+            step(row, c);                                                                         \
+            ka = chunk_at<NIN, NOUT>(row, c, i + 1 < n, g, gp, gop, op, WEIGHT(row));  \
+            load_chunk(A, ka, voff);                                                              \
+            BODY(B, kb);                                                                          \
+            step(row, c);                                                                         \
+            kb = chunk_at<NIN, NOUT>(row, c, i + 2 < n, g, gp, gop, op, WEIGHT(row));  \
+            load_chunk(B, kb, voff);                                                              \
+            BODY(A, ka);                                                                          \
+        }                                                                                         \
+        if (i < n) {                                                                              \
+            BODY(B, kb);                                                                          \
+        }                                                                                         \
+    }
+
+// Forward, flat mapping: wavefront w takes chunks w k .. w k + k - 1 of the
+// `total` chunks of the tensor.
+template <int IO, bool LB, bool FAST, bool RWB>
+__global__ void __launch_bounds__(256)
+situ_glu_fwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride, void *__restrict__ out, uint32_t total, ChunkGeom g, GateK gk, UpK uk)
+{
+    const uint32_t voff = (threadIdx.x & 63) * 16u;
+    const uint32_t gw = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t first = gw * (uint32_t)g.k;
+    if (first >= total)
+        return;
+    const int n = total - first < (uint32_t)g.k ? (int)(total - first) : g.k;
+    int64_t row;
+    uint32_t c;
+    locate(first, g, row, c);
+    auto step = [&](int64_t &r_, uint32_t &c_) {
+        if (++c_ == (uint32_t)g.cpr) {
+            c_ = 0;
+            ++r_;
+        }
+    };
+    const char *gp = static_cast<const char *>(gate_up);
+    const char *gop = nullptr;
+    char *op = static_cast<char *>(out);
+#define SITU_FWD_BODY(R, K) fwd_chunk<IO, LB, FAST, RWB>(R, K, voff, gk, uk)
+#define SITU_WEIGHT(R) weight_bits<RWB>(rw, (R) * rw_stride)
+    SITU_CHUNK_PIPELINE(2, 1, SITU_WEIGHT, SITU_FWD_BODY)
+#undef SITU_WEIGHT
+#undef SITU_FWD_BODY
+}
+
+// Backward without a routing-weight gradient, flat mapping.
+template <int IO, bool LB, bool FAST, bool RWB>
+__global__ void __launch_bounds__(256, LB || RWB ? 6 : 8)
+situ_glu_bwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
+                    uint32_t total, ChunkGeom g, GateK gk, UpK uk)
+{
+    const uint32_t voff = (threadIdx.x & 63) * 16u;
+    const uint32_t gw = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t first = gw * (uint32_t)g.k;
+    if (first >= total)
+        return;
+    const int n = total - first < (uint32_t)g.k ? (int)(total - first) : g.k;
+    int64_t row;
+    uint32_t c;
+    locate(first, g, row, c);
+    auto step = [&](int64_t &r_, uint32_t &c_) {
+        if (++c_ == (uint32_t)g.cpr) {
+            c_ = 0;
+            ++r_;
+        }
+    };
+    const char *gp = static_cast<const char *>(gate_up);
+    const char *gop = static_cast<const char *>(grad_out);
+    char *op = static_cast<char *>(d_gate_up);
+    float acc = 0.0f;
+#define SITU_BWD_BODY(R, K) bwd_chunk<IO, LB, FAST, RWB, false>(R, K, voff, gk, uk, acc)
+#define SITU_WEIGHT(R) weight_bits<RWB>(rw, (R) * rw_stride)
+    SITU_CHUNK_PIPELINE(3, 2, SITU_WEIGHT, SITU_BWD_BODY)
+#undef SITU_WEIGHT
+#undef SITU_BWD_BODY
+}
+
+// Backward with the routing-weight gradient, row mapping: workgroup b holds
+// rows b rpb .. b rpb + rpb - 1, wpr wavefronts each; wavefront j of a row
+// takes its chunks j k .. j k + k - 1.  The row's wavefronts add their
+// partial sums in LDS in wavefront order (deterministic).  One weight per
+// row: d_rw[row]; one weight for all rows: the row's partial goes to
+// row_partials[row] for the fixed-order second pass.
+template <int IO, bool LB, bool FAST, bool RWB>
+__global__ void __launch_bounds__(1024, LB || RWB ? 6 : 8)
+situ_glu_bwd_dr_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
+                       void *__restrict__ d_rw, float *__restrict__ row_partials, int64_t rows, ChunkGeom g,
+                       GateK gk, UpK uk)
+{
+    __shared__ float wave_part[kMaxWaves];
+    const uint32_t voff = (threadIdx.x & 63) * 16u;
+    const int lane = threadIdx.x & 63;
+    const int slot = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rpb = (int)(blockDim.x >> 6) / g.wpr;
+    const int rib = (slot * (int)g.wmagic) >> 8;  // slot / wpr
+    const int grp = slot - rib * g.wpr;
+    int64_t row = (int64_t)blockIdx.x * rpb + rib;
+    const bool live = row < rows;
+    const uint32_t c0 = (uint32_t)grp * (uint32_t)g.k;
+    float acc = 0.0f;
+    if (live && c0 < (uint32_t)g.cpr) {
+        const int n = (uint32_t)g.cpr - c0 < (uint32_t)g.k ? (int)((uint32_t)g.cpr - c0) : g.k;
+        uint32_t c = c0;
+        auto step = [&](int64_t &, uint32_t &c_) { ++c_; };
+        const char *gp = static_cast<const char *>(gate_up);
+        const char *gop = static_cast<const char *>(grad_out);
+        char *op = static_cast<char *>(d_gate_up);
+        const uint32_t rb = weight_bits<RWB>(rw, row * rw_stride);  // one row: one weight
+#define SITU_BWD_BODY(R, K) bwd_chunk<IO, LB, FAST, RWB, true>(R, K, voff, gk, uk, acc)
+#define SITU_WEIGHT(R) rb
+        SITU_CHUNK_PIPELINE(3, 2, SITU_WEIGHT, SITU_BWD_BODY)
+#undef SITU_WEIGHT
+#undef SITU_BWD_BODY
+    }
+    const float scale = LB ? gk.beta1 * uk.beta2 : gk.beta1;
+    const float s = wave_sum(acc);
+    if (g.wpr == 1) {
+        if (live && lane == 0)
+            write_row_dr(s * scale, row, rw_stride, RWB, d_rw, row_partials);
+    } else {
+        if (lane == 0)
+            wave_part[slot] = s;
+        __syncthreads();
+        if (live && grp == 0 && lane == 0) {
+            float t = 0.0f;
+            for (int w = 0; w < g.wpr; ++w)
+                t += wave_part[slot + w];
+            write_row_dr(t * scale, row, rw_stride, RWB, d_rw, row_partials);
         }
     }
 }
 
 // Element path (any alignment, any intermediate): one wavefront per row.
 template <int IO, bool LB, bool FAST>
-__global__ void __launch_bounds__(64 * kMaxWaves)
+__global__ void __launch_bounds__(256)
 situ_glu_fwd_elem_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
                          int64_t rw_stride, void *__restrict__ out, int64_t rows, int inter, int /*unused*/,
                          GateK gk, UpK uk)
@@ -196,7 +325,7 @@ situ_glu_fwd_elem_kernel(const void *__restrict__ gate_up, const void *__restric
 }
 
 template <int IO, bool LB, bool FAST, bool DR>
-__global__ void __launch_bounds__(64 * kMaxWaves)
+__global__ void __launch_bounds__(256)
 situ_glu_bwd_elem_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
                          int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
                          void *__restrict__ d_rw, float *__restrict__ row_partials, int64_t rows, int inter,
@@ -268,65 +397,68 @@ __global__ void situ_glu_zero_kernel(unsigned char *__restrict__ p, int64_t n)
 
 // ---------------------------------------------------------------- dispatch
 
-using FwdFn = void (*)(const void *, const void *, int, int64_t, void *, int64_t, int, int, GateK, UpK);
-using BwdFn = void (*)(const void *, const void *, int, int64_t, const void *, void *, void *, float *,
-                       int64_t, int, int, GateK, UpK);
+using FwdFn = void (*)(const void *, const void *, int64_t, void *, uint32_t, ChunkGeom, GateK, UpK);
+using BwdFn = void (*)(const void *, const void *, int64_t, const void *, void *, uint32_t, ChunkGeom, GateK, UpK);
+using BwdDrFn = void (*)(const void *, const void *, int64_t, const void *, void *, void *, float *, int64_t,
+                         ChunkGeom, GateK, UpK);
+using FwdElemFn = void (*)(const void *, const void *, int, int64_t, void *, int64_t, int, int, GateK, UpK);
+using BwdElemFn = void (*)(const void *, const void *, int, int64_t, const void *, void *, void *, float *,
+                           int64_t, int, int, GateK, UpK);
 
-template <int IO, bool VEC, bool LB, bool FAST>
-constexpr FwdFn fwd_fn()
-{
-    if constexpr (VEC)
-        return situ_glu_fwd_vec_kernel<IO, LB, FAST>;
-    else
-        return situ_glu_fwd_elem_kernel<IO, LB, FAST>;
-}
-template <int IO, bool VEC, bool LB, bool FAST, bool DR>
-constexpr BwdFn bwd_fn()
-{
-    if constexpr (VEC)
-        return situ_glu_bwd_vec_kernel<IO, LB, FAST, DR>;
-    else
-        return situ_glu_bwd_elem_kernel<IO, LB, FAST, DR>;
-}
+// index: [io][rw bf16][lb * 2 + fast]
+#define SITU_BY_LB_FAST(K, IO, RWB) {K<IO, false, false, RWB>, K<IO, false, true, RWB>, \
+                                     K<IO, true, false, RWB>, K<IO, true, true, RWB>}
+#define SITU_BY_IO_RW(K) {{SITU_BY_LB_FAST(K, IO_F32, false), SITU_BY_LB_FAST(K, IO_F32, true)}, \
+                          {SITU_BY_LB_FAST(K, IO_BF16, false), SITU_BY_LB_FAST(K, IO_BF16, true)}}
+const FwdFn kFwd[2][2][4] = SITU_BY_IO_RW(situ_glu_fwd_kernel);
+const BwdFn kBwd[2][2][4] = SITU_BY_IO_RW(situ_glu_bwd_kernel);
+const BwdDrFn kBwdDr[2][2][4] = SITU_BY_IO_RW(situ_glu_bwd_dr_kernel);
+#define SITU_ELEM(K, IO, ...) {K<IO, false, false __VA_ARGS__>, K<IO, false, true __VA_ARGS__>, \
+                               K<IO, true, false __VA_ARGS__>, K<IO, true, true __VA_ARGS__>}
+// index: [io][lb * 2 + fast]
+const FwdElemFn kFwdElem[2][4] = {SITU_ELEM(situ_glu_fwd_elem_kernel, IO_F32), SITU_ELEM(situ_glu_fwd_elem_kernel, IO_BF16)};
+// index: [io][dr][lb * 2 + fast]
+const BwdElemFn kBwdElem[2][2][4] = {
+    {SITU_ELEM(situ_glu_bwd_elem_kernel, IO_F32, , false), SITU_ELEM(situ_glu_bwd_elem_kernel, IO_F32, , true)},
+    {SITU_ELEM(situ_glu_bwd_elem_kernel, IO_BF16, , false), SITU_ELEM(situ_glu_bwd_elem_kernel, IO_BF16, , true)}};
 
-#define SITU_FWD_ROW(IO, VEC)                                                                  \
-    { fwd_fn<IO, VEC, false, false>(), fwd_fn<IO, VEC, false, true>(),                        \
-      fwd_fn<IO, VEC, true, false>(), fwd_fn<IO, VEC, true, true>() }
-// index: [io][vec][lb * 2 + fast]
-const FwdFn kFwd[2][2][4] = {
-    {SITU_FWD_ROW(IO_F32, false), SITU_FWD_ROW(IO_F32, true)},
-    {SITU_FWD_ROW(IO_BF16, false), SITU_FWD_ROW(IO_BF16, true)},
-};
-#define SITU_BWD_ROW(IO, VEC, DR)                                                              \
-    { bwd_fn<IO, VEC, false, false, DR>(), bwd_fn<IO, VEC, false, true, DR>(),                \
-      bwd_fn<IO, VEC, true, false, DR>(), bwd_fn<IO, VEC, true, true, DR>() }
-// index: [io][vec][dr][lb * 2 + fast]
-const BwdFn kBwd[2][2][2][4] = {
-    {{SITU_BWD_ROW(IO_F32, false, false), SITU_BWD_ROW(IO_F32, false, true)},
-     {SITU_BWD_ROW(IO_F32, true, false), SITU_BWD_ROW(IO_F32, true, true)}},
-    {{SITU_BWD_ROW(IO_BF16, false, false), SITU_BWD_ROW(IO_BF16, false, true)},
-     {SITU_BWD_ROW(IO_BF16, true, false), SITU_BWD_ROW(IO_BF16, true, true)}},
-};
+// Element path: one wavefront per row, four rows per workgroup.
+constexpr int kElemRowsPerBlock = 4;
 
 }  // namespace
 
 int launch_fwd(const FwdLaunch &L, void *stream)
 {
-    const Shape sh = shape(L.rows, L.inter, L.io, L.vec, L.rows_per_block, kUnrollFwd);
-    const FwdFn fn = kFwd[L.io][L.vec][L.lb * 2 + L.fast];
-    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up, L.rw, L.rw_bf16,
-                       L.rw_stride, L.out, L.rows, L.inter, sh.waves_per_row, L.gk, L.uk);
+    const int v = L.lb * 2 + L.fast;
+    if (L.vec) {
+        hipLaunchKernelGGL(kFwd[L.io][L.rw_bf16][v], dim3(L.split.grid), dim3(L.split.block), 0, (hipStream_t)stream,
+                           L.gate_up, L.rw, L.rw_stride, L.out, L.split.total, L.split.geom, L.gk, L.uk);
+    } else {
+        const unsigned grid = (unsigned)((L.rows + kElemRowsPerBlock - 1) / kElemRowsPerBlock);
+        hipLaunchKernelGGL(kFwdElem[L.io][v], dim3(grid), dim3(64 * kElemRowsPerBlock), 0, (hipStream_t)stream,
+                           L.gate_up, L.rw, L.rw_bf16, L.rw_stride, L.out, L.rows, L.inter, 0, L.gk, L.uk);
+    }
     return (int)hipGetLastError();
 }
 
 int launch_bwd(const BwdLaunch &L, void *stream)
 {
-    const Shape sh = shape(L.rows, L.inter, L.io, L.vec, L.rows_per_block, kUnrollBwd);
+    const int v = L.lb * 2 + L.fast;
     const int dr = L.d_rw != nullptr;
-    const BwdFn fn = kBwd[L.io][L.vec][dr][L.lb * 2 + L.fast];
-    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up, L.rw, L.rw_bf16,
-                       L.rw_stride, L.grad_out, L.d_gate_up, L.d_rw, L.row_partials, L.rows, L.inter,
-                       sh.waves_per_row, L.gk, L.uk);
+    if (L.vec && dr) {
+        hipLaunchKernelGGL(kBwdDr[L.io][L.rw_bf16][v], dim3(L.split.grid), dim3(L.split.block), 0,
+                           (hipStream_t)stream, L.gate_up, L.rw, L.rw_stride, L.grad_out, L.d_gate_up, L.d_rw,
+                           L.row_partials, L.rows, L.split.geom, L.gk, L.uk);
+    } else if (L.vec) {
+        hipLaunchKernelGGL(kBwd[L.io][L.rw_bf16][v], dim3(L.split.grid), dim3(L.split.block), 0, (hipStream_t)stream,
+                           L.gate_up, L.rw, L.rw_stride, L.grad_out, L.d_gate_up, L.split.total, L.split.geom, L.gk,
+                           L.uk);
+    } else {
+        const unsigned grid = (unsigned)((L.rows + kElemRowsPerBlock - 1) / kElemRowsPerBlock);
+        hipLaunchKernelGGL(kBwdElem[L.io][dr][v], dim3(grid), dim3(64 * kElemRowsPerBlock), 0, (hipStream_t)stream,
+                           L.gate_up, L.rw, L.rw_bf16, L.rw_stride, L.grad_out, L.d_gate_up, L.d_rw, L.row_partials,
+                           L.rows, L.inter, 0, L.gk, L.uk);
+    }
     int err = (int)hipGetLastError();
     if (err == 0 && dr && L.rw_stride == 0)
         err = launch_dr_reduce(L.row_partials, L.rows, L.d_rw, L.rw_bf16, stream);

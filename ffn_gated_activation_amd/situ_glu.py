@@ -418,15 +418,29 @@ def situ_glu_last_error() -> str:
     return _capi.last_error()
 
 
+def situ_glu_split(io_dtype: torch.dtype, rows: int, intermediate: int, linear_beta_given: bool,
+                   direction: int) -> dict:
+    """The 128-bit path's work split for a call with these sizes (host only):
+    direction 0 forward, 1 backward, 2 backward with d_routing_weights."""
+    import ctypes
+    lib = _capi.load()
+    out = (ctypes.c_int64 * 10)()
+    _capi.check(lib.situ_glu_split(_DT[io_dtype], int(rows), int(intermediate), int(bool(linear_beta_given)),
+                                   int(direction), out), lib)
+    keys = ("chunks_per_row", "chunks", "chunks_per_wave", "waves_per_row", "workgroups", "threads",
+            "magic", "shift", "slot_magic", "half_row_bytes")
+    return dict(zip(keys, (int(v) for v in out)))
+
+
 def situ_glu_abi_version() -> int:
     return int(_capi.load().situ_glu_abi_version())
 
 
 def situ_glu_gate_window(beta: float = 4.0):
-    """(G*_f32, cubic half width, c0, c1, c2, c3, quadratic half width): the
-    constants the kernels use near the root of dT_g/dG."""
+    """(G*_f32, cubic half width, c0, c1, c2, c3, bf16 value nearest G*,
+    dT_g/dG there): the constants the kernels use near the root of dT_g/dG."""
     import ctypes
     lib = _capi.load()
-    out = (ctypes.c_float * 7)()
+    out = (ctypes.c_float * 8)()
     _capi.check(lib.situ_glu_gate_window(float(beta), out), lib)
     return tuple(float(v) for v in out)

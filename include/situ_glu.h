@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SITU_GLU_ABI_VERSION 7
+#define SITU_GLU_ABI_VERSION 8
 
 /* return codes */
 #define SITU_OK 0
@@ -432,12 +432,33 @@ int situ_glu_abi_version(void);
  * section "Activation": T_g has its minimum at G*), so inside
  * |G - out[0]| <= out[1] the fp32-io kernels evaluate dT_g/dG as
  * out[2] + out[3] d + out[4] d^2 + out[5] d^3 with d = G - out[0]
- * (out[0] = G* rounded to fp32), and inside |G - out[0]| <= out[6] the
- * bf16-io kernels evaluate out[2] + out[3] d + out[4] d^2.  out must hold 7
- * floats.
+ * (out[0] = G* rounded to fp32).  The bf16-io kernels, whose inputs are bf16
+ * values, take dT_g/dG = out[7] at the one bf16 input G = out[6] nearest G*
+ * (the only bf16 value where the cancellation costs more than ~3e-5 relative)
+ * and the plain formula elsewhere.  out must hold 8 floats.
  * Returns SITU_OK or SITU_ERR_INVALID_ARG (bad beta, NULL out).
  */
 int situ_glu_gate_window(double beta, float *out);
+
+/*
+ * Diagnostic: the work split of the 128-bit path for a call with these sizes
+ * (host only, no device work).  direction: 0 situ_glu_fwd, 1 situ_glu_bwd
+ * without d_routing_weights, 2 with it.  A chunk is 64 lanes x 16 bytes
+ * (1 KiB) of each half row; out must hold 10 int64:
+ *   out[0] chunks per row, out[1] chunks of the tensor, out[2] chunks per
+ *   wavefront, out[3] wavefronts per row (direction 2; else 0: chunks are
+ *   numbered over the whole tensor), out[4] workgroups, out[5] threads per
+ *   workgroup, out[6], out[7] the multiplier and shift that divide a chunk
+ *   index by out[0] (index / out[0] = (index * out[6]) >> (32 + out[7]) for
+ *   index < 2^31), out[8] the multiplier that divides a wavefront slot by
+ *   out[3] ((slot * out[8]) >> 8 for slot < 16), out[9] bytes of a half row.
+ * Returns SITU_OK; SITU_ERR_INVALID_ARG for a bad dtype or direction, NULL
+ * out, sizes out of range, or sizes that take the element path (I times the
+ * element size not a multiple of 16); SITU_ERR_UNSUPPORTED beyond 2^31
+ * chunks.
+ */
+int situ_glu_split(int io_dtype, int64_t rows, int64_t intermediate,
+                   int linear_beta_given, int direction, int64_t *out);
 
 #ifdef __cplusplus
 }

@@ -59,15 +59,15 @@ def _small_arg(y: np.ndarray) -> np.ndarray:
 
 
 def grad_error_bounds(gate_up64: np.ndarray, dgu64: np.ndarray, dg_scale64: np.ndarray, beta: float, linear_beta,
-                      io_bf16: bool, window=None) -> tuple[np.ndarray, np.ndarray]:
+                      io_bf16: bool) -> tuple[np.ndarray, np.ndarray]:
     """Absolute bounds on the backward's fp32 dG and dU (before any output
     rounding).  fp32 io: the 1e-5 bar of the fp32 backward (dG relative to the
     sum of the magnitudes of dT_g/dG's two terms, dg_scale).  bf16 io adds the
     kernels' cheaper pieces: dG carries T_u and dU carries T_g, each with the
-    small-argument error of its 1 - exp(-y) (y = 2|U|/linear_beta, 2|G|/beta);
-    inside the window (G*_f32, half width) around the gate's minimum dT_g/dG
-    is a quadratic whose dropped term is below 1e-4 of the linear one, counted
-    here as 1e-4 dg_scale."""
+    small-argument error of its 1 - exp(-y) (y = 2|U|/linear_beta, 2|G|/beta).
+    Near the gate's minimum the kernels take the exact dT_g/dG at the one bf16
+    input nearest the root, and elsewhere the plain formula's rounding stays
+    inside the 1e-5 dg_scale term."""
     inter = gate_up64.shape[1] // 2
     G, U = gate_up64[:, :inter], gate_up64[:, inter:]
     dG, dU = np.abs(dgu64[:, :inter]), np.abs(dgu64[:, inter:])
@@ -77,9 +77,6 @@ def grad_error_bounds(gate_up64: np.ndarray, dgu64: np.ndarray, dg_scale64: np.n
         if linear_beta is not None:
             eg = eg + _small_arg(2.0 * np.abs(U) / linear_beta) * dG
         eu = eu + _small_arg(2.0 * np.abs(G) / beta) * dU
-        if window is not None:
-            g0, hw = window
-            eg = eg + np.where(np.abs(G - g0) <= hw, 1e-4 * dg_scale64, 0.0)
     return eg, eu
 
 

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib, capi):
     assert set(names) == set(capi.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 7
+    assert lib.situ_glu_abi_version() == capi.ABI_VERSION == 8
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -395,16 +395,26 @@ def test_python_layer_rejects_cpu_tensors():
         situ_glu_fwd(torch.zeros(2, 8), torch.ones(2, 1))
 
 
+def _bf16_neighbours(x: float, n: int) -> np.ndarray:
+    """The 2n+1 bf16 values around the bf16 value x (bit patterns +-n)."""
+    b = int(np.float32(x).view(np.uint32)) >> 16
+    bits = np.arange(b - n, b + n + 1, dtype=np.uint32) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
 def test_gate_window_constants(capi, lib):
     """The root window the kernels use agrees with the oracle: G*_f32 is the
-    float nearest the oracle's root, the cubic (fp32 io) matches the oracle's
-    dT_g/dG inside its window to 1e-6 relative and the quadratic (bf16 io)
-    inside its window to 1e-4 (the polynomials evaluated in double)."""
+    float nearest the oracle's root and the cubic (fp32 io) matches the
+    oracle's dT_g/dG inside its window to 1e-6 relative (evaluated in
+    double).  bf16 io: out[6] is the bf16 value nearest the root, out[7] the
+    oracle's dT_g/dG there to fp32 rounding, and at every other bf16 value
+    within 64 values of it the plain formula's two terms cancel by at most a
+    factor 600 (so its fp32 rounding stays ~1e-4 of a bf16 ulp)."""
     import oracle
-    out = (ctypes.c_float * 7)()
+    out = (ctypes.c_float * 8)()
     for beta in (4.0, 3.0, 1.0, 0.5, 2.0, 100.0, 1e4):
         assert lib.situ_glu_gate_window(beta, out) == 0
-        ghi, hw, c0, c1, c2, c3, hw2 = [float(v) for v in out]
+        ghi, hw, c0, c1, c2, c3, gsub, tsub = [float(v) for v in out]
         lo, hi = -80.0, -1e-4
         for _ in range(200):
             mid = 0.5 * (lo + hi)
@@ -423,16 +433,77 @@ def test_gate_window_constants(capi, lib):
             # coefficients are rounded to fp32: allow their rounding too
             tol = 1e-6 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d) + abs(c3 * d ** 3))
             assert abs(p - t) <= tol, (beta, d, p, t)
-        # the bf16 kernels' quadratic: within 1e-4 of the term scale inside hw2
-        assert 0 < hw2 <= hw
-        for d in np.linspace(-hw2, hw2, 41):
-            g = ghi + d
-            p2 = c0 + d * (c1 + d * c2)
-            t = oracle.gate_grad(g, beta)
-            scale = abs(c1 * (g - root)) + 1e-300
-            tol = 1e-4 * scale + 6e-8 * (abs(c0) + abs(c1 * d) + abs(c2 * d * d))
-            assert abs(p2 - t) <= tol, (beta, d, p2, t)
+        # bf16 io: the substituted value and its neighbours
+        near = _bf16_neighbours(gsub, 64)
+        assert np.all(np.abs(near - root) >= abs(gsub - root)), (beta, gsub, root)
+        t = oracle.gate_grad(gsub, beta)
+        assert abs(tsub - t) <= 2.0 ** -23 * abs(t) + 1e-45, (beta, tsub, t)
+        for g in near:
+            if g == gsub or g >= 0:
+                continue
+            # G < 0: T_g' = sigmoid sech^2(G/b) - b tanh(|G|/b) sigmoid sigmoid(-G), terms of opposite sign
+            s = 1.0 / (1.0 + np.exp(-g))
+            t1 = s / np.cosh(g / beta) ** 2
+            t2 = beta * np.tanh(-g / beta) * s * (1.0 - s)
+            assert (t1 + t2) / abs(t1 - t2) <= 600.0, (beta, g, (t1 + t2) / abs(t1 - t2))
     assert lib.situ_glu_gate_window(-1.0, out) == capi.SITU_ERR_INVALID_ARG
+
+
+def test_split_covers_every_chunk(lib, capi):
+    """The 128-bit path's work split (situ_glu_split): the chunk-index
+    division by chunks per row is exact for every chunk index of the
+    workloads' shapes and for sampled indices up to 2^31 at many other
+    divisors; the flat grid covers every chunk once; the row mapping gives
+    each row at most 16 wavefronts that cover its chunks, and the slot
+    division is exact for every slot of a workgroup."""
+    out = (ctypes.c_int64 * 10)()
+    rng = np.random.default_rng(0)
+    shapes = [(256, 512, capi.SITU_DTYPE_F32), (8192, 2048, capi.SITU_DTYPE_BF16),
+              (16384, 18432, capi.SITU_DTYPE_BF16), (65536, 2048, capi.SITU_DTYPE_BF16),
+              (131072, 2048, capi.SITU_DTYPE_BF16), (7, 8, capi.SITU_DTYPE_BF16), (3, 4, capi.SITU_DTYPE_F32),
+              (5, 520, capi.SITU_DTYPE_BF16), (1000, 65536 + 8, capi.SITU_DTYPE_BF16),
+              (2, 1 << 20, capi.SITU_DTYPE_F32), (3, (1 << 28) - 8, capi.SITU_DTYPE_BF16)]
+    for rows, inter, dt in shapes:
+        es = 4 if dt == capi.SITU_DTYPE_F32 else 2
+        for lbg in (0, 1):
+            for direction in (0, 1, 2):
+                assert lib.situ_glu_split(dt, rows, inter, lbg, direction, out) == 0, capi.last_error(lib)
+                cpr, total, k, wpr, grid, block, magic, shift, wmagic, half = [int(v) for v in out]
+                assert half == inter * es and cpr == -(-half // 1024) and total == rows * cpr
+                if cpr > 1:
+                    x = np.arange(total, dtype=np.uint64) if total <= 1 << 22 else \
+                        rng.integers(0, total, 1 << 20, dtype=np.uint64)
+                    q = (x * np.uint64(magic)) >> np.uint64(32 + shift)
+                    assert np.array_equal(q, x // np.uint64(cpr)), (rows, inter, direction)
+                assert 64 <= block <= 1024 and block % 64 == 0
+                if direction < 2:
+                    assert wpr == 0 and block <= 256
+                    waves = grid * (block // 64)
+                    assert waves * k >= total and (waves - block // 64) * k < total
+                else:
+                    assert 1 <= wpr <= 16 and wpr * k >= cpr and (wpr - 1) * k < cpr
+                    rpb = block // 64 // wpr
+                    assert rpb >= 1 and rpb * wpr == block // 64
+                    assert grid * rpb >= rows and (grid - 1) * rpb < rows
+                    for slot in range(16):
+                        assert (slot * wmagic) >> 8 == slot // wpr
+    # the division at other divisors, up to the largest chunk index 2^31 - 1
+    for cpr in list(range(2, 300)) + [int(v) for v in rng.integers(300, 1 << 20, 200)]:
+        inter = cpr * 512
+        rows = max(1, ((1 << 31) - 1) // cpr)
+        assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, rows, inter, 1, 0, out) == 0, capi.last_error(lib)
+        magic, shift = int(out[6]), int(out[7])
+        x = np.concatenate([rng.integers(0, rows * cpr, 4096, dtype=np.uint64),
+                            np.array([0, cpr - 1, cpr, rows * cpr - 1], dtype=np.uint64),
+                            (np.arange(1, 64, dtype=np.uint64) * np.uint64(cpr)) - np.uint64(1)])
+        q = (x * np.uint64(magic)) >> np.uint64(32 + shift)
+        assert np.array_equal(q, x // np.uint64(cpr)), cpr
+    # rejected: element-path sizes, bad direction, too many chunks
+    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 12, 1, 0, out) == capi.SITU_ERR_INVALID_ARG
+    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 16, 1, 3, out) == capi.SITU_ERR_INVALID_ARG
+    assert lib.situ_glu_split(7, 4, 16, 1, 0, out) == capi.SITU_ERR_INVALID_ARG
+    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 16, 1, 0, None) == capi.SITU_ERR_INVALID_ARG
+    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, (1 << 31) - 1, 1024, 1, 0, out) == capi.SITU_ERR_UNSUPPORTED
 
 
 def test_mx_python_layer_rejects():

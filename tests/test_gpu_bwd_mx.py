@@ -37,7 +37,7 @@ def _say(msg):
 
 
 def _check(gate_up, rw, grad_out, beta, lb, fmt, mode, want_drw=True, rows=None, tag=""):
-    from ffn_gated_activation_amd import situ_glu_bwd_mxfp8, situ_glu_gate_window
+    from ffn_gated_activation_amd import situ_glu_bwd_mxfp8
     _say(f"[mx-bwd] {tag} gate_up={tuple(gate_up.shape)} {gate_up.dtype} rw={tuple(rw.shape)} {fmt}/{mode} "
          f"drw={want_drw}")
     codes, scales, drw = situ_glu_bwd_mxfp8(gate_up, rw, grad_out, beta, lb, want_drw, fmt, mode)
@@ -58,9 +58,7 @@ def _check(gate_up, rw, grad_out, beta, lb, fmt, mode, want_drw=True, rows=None,
     gu64, go64, r64 = host_f64(gu), host_f64(go), host_f64(r)
     b = oracle.backward(gu64, r64, go64, beta, lb, want_dr=want_drw, want_scales=True, threads=threads())
     dgu = b["d_gate_up"]
-    w = situ_glu_gate_window(beta)
-    eg, eu = grad_error_bounds(gu64, dgu, b["dg_scale"], beta, lb, gate_up.dtype == torch.bfloat16,
-                               window=(w[0], w[6]))
+    eg, eu = grad_error_bounds(gu64, dgu, b["dg_scale"], beta, lb, gate_up.dtype == torch.bfloat16)
     al = subnormal_allowance(gu64, r64, go64, beta, lb)
     zero = np.zeros_like(eg)
     st_g = assert_mx_window(f"{tag} dG", c[:, :inter], s[:, :nblk], dgu[:, :inter], zero, eg + al["dG"], fmt, mode)
