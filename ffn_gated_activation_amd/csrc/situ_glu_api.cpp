@@ -264,6 +264,8 @@ UpK make_up_consts(double beta2)
     UpK k{};
     k.beta2 = (float)beta2;
     k.ku = (float)(2.0L / (long double)beta2 * 1.4426950408889634073599L);
+    k.inv_b2 = (float)(1.0L / (long double)beta2);
+    k.small_max = (float)(0.25L * (long double)beta2);
     return k;
 }
 

@@ -197,6 +197,28 @@ __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const 
     }
 }
 
+// tanh(x) for |x| <= 1/4: the odd Taylor polynomial through x^9 (tanh's
+// series x - x^3/3 + 2x^5/15 - 17x^7/315 + 62x^9/2835 - ...; the first term
+// dropped is below 1e-8 of tanh there; fp32 evaluation adds ~3 ulp).  No
+// exponential, no reciprocal, no cancellation for small x.
+__device__ __forceinline__ float tanh_small(float x)
+{
+    const float x2 = x * x;
+    const float p = fmaf(fmaf(fmaf(62.0f / 2835.0f, x2, -17.0f / 315.0f), x2, 2.0f / 15.0f), x2, -1.0f / 3.0f);
+    return fmaf(x * x2, p, x);
+}
+
+// Forward with the up branch as tanh_small(U / b2) (bf16 io, |U| <= b2 / 4):
+// one reciprocal of (1 + e1)(1 + e2) only.
+template <bool FAST>
+__device__ __forceinline__ float fwd_elem_small_u(float g, float u, float rscale, const GateK &gk, const UpK &uk)
+{
+    const Gate t = gate_parts<FAST, false>(g, rscale, gk);
+    const float a = 1.0f + t.e1;
+    const float q = rcp(fmaf(t.e2, a, a));  // 1 / ((1 + e1)(1 + e2))
+    return (t.nt * t.sn_s) * (tanh_small(u * uk.inv_b2) * q);
+}
+
 // dT_g/dG / 4 near its root, where its two terms cancel.  fp32 io: the
 // cubic in d = G - G*_f32 inside the window.  bf16 io: G is a bf16 value, and
 // only the one nearest the root loses more than ~3e-5 to the cancellation;
@@ -262,6 +284,44 @@ __device__ __forceinline__ BwdOut bwd_elem(float g, float u, float go, float cG,
         o.dg = go * u * tgp * cG;
     }
     return o;
+}
+
+// Backward with the up branch as t = tanh_small(U / b2) (bf16 io,
+// |U| <= b2 / 4): T_u = b2 t, T_u' = 1 - t^2, and with q = 1 / ((1 + e1)(1 + e2)):
+//   go T_g T_u / (b1 b2) = go a1 q t,  dU = go a1 q (1 - t^2) cU / 4,
+//   dG = go t (T_g' / 4) cG,  T_g' / 4 = |sn| br q^2.
+// FOLD: cU / 4 rides on nt (no routing-weight gradient).
+template <bool FAST, bool FOLD>
+__device__ __forceinline__ BwdOut bwd_elem_small_u(float g, float u, float go, float cG, float cU4, const GateK &gk,
+                                                   const UpK &uk)
+{
+    BwdOut o;
+    const Gate t = gate_parts<FAST, false>(g, FOLD ? cU4 : 1.0f, gk);
+    const float om = FAST ? 1.0f - t.e2 : (0.25f * gk.beta1) * fmaf(-t.e1, t.e1, 1.0f);
+    const float e1B = fmaf(t.e1, t.e2, t.e1);
+    const float br = fmaf(om, t.snc_s, e1B);
+    const float sbr = fabsf(t.sn_s) * br;
+    const float q = rcp((1.0f + t.e2) + e1B);
+    const float tgp = gate_grad4_window<false>(g, sbr * (q * q), gk);
+    const float tu = tanh_small(u * uk.inv_b2);
+    const float s2 = fmaf(-tu, tu, 1.0f);
+    const float gqa = (go * q) * (t.nt * t.sn_s);
+    o.p = gqa * tu;
+    o.du = FOLD ? gqa * s2 : gqa * s2 * cU4;
+    o.dg = go * tu * tgp * cG;
+    return o;
+}
+
+// True on every lane when no |U| of the wavefront's values exceeds the
+// polynomial's range (NaN counts as in range: it propagates either way).
+template <int E>
+__device__ __forceinline__ bool wave_up_small(const float *u, const UpK &uk)
+{
+    float m = fabsf(u[0]);
+#pragma unroll
+    for (int e = 1; e < E; ++e)
+        m = fmaxf(m, fabsf(u[e]));
+    return __builtin_amdgcn_ballot_w64(!(m <= uk.small_max) && m == m) == 0;
 }
 
 // ---------------------------------------------------------------- reductions

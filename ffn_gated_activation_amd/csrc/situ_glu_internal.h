@@ -28,11 +28,15 @@ struct GateK {
     float gsub, tsub;
 };
 
-// Up-branch constant (only used when linear_beta is given):
+// Up-branch constants (only used when linear_beta is given):
 //   v = exp(-2|U|/b2) = exp2(-|U| * ku)
+// and for the bf16-io kernels' polynomial tanh(U/b2), valid for
+// |U| <= small_max = b2/4: x = U * inv_b2.
 struct UpK {
     float beta2;
     float ku;
+    float inv_b2;
+    float small_max;
 };
 
 enum { IO_F32 = 0, IO_BF16 = 1 };

@@ -88,15 +88,24 @@ __device__ __forceinline__ Chunk<NIN, NOUT> chunk_at(int64_t row, uint32_t c, bo
     return k;
 }
 
-// Issue one chunk's loads.  The scheduling fences keep each chunk's loads
-// ahead of the previous chunk's math, as written.
+// Fences that keep each chunk's loads ahead of the previous chunk's math, as
+// written: the scheduling barrier within a block, and an empty statement
+// that may touch memory, so that no load is sunk past a branch of the math
+// (it emits no instruction).
+__device__ __forceinline__ void order_fence()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// Issue one chunk's loads.
 template <int NIN, int NOUT>
 __device__ __forceinline__ void load_chunk(uint4 *v, const Chunk<NIN, NOUT> &k, uint32_t voff)
 {
 #pragma unroll
     for (int i = 0; i < NIN; ++i)
         v[i] = bload(k.in[i], voff);
-    __builtin_amdgcn_sched_barrier(0);
+    order_fence();
 }
 
 template <int IO, bool LB, bool FAST, bool RWB>
@@ -110,11 +119,17 @@ __device__ __forceinline__ void fwd_chunk(const uint4 *v, const Chunk<2, 1> &k, 
     float g[E], u[E], y[E];
     T::unpack(v[0], g);
     T::unpack(v[1], u);
+    if (LB && IO == IO_BF16 && wave_up_small<E>(u, uk)) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        y[e] = fwd_elem<LB, FAST, IO == IO_F32>(g[e], u[e], rscale, gk, uk);
+        for (int e = 0; e < E; ++e)
+            y[e] = fwd_elem_small_u<FAST>(g[e], u[e], rscale, gk, uk);
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            y[e] = fwd_elem<LB, FAST, IO == IO_F32>(g[e], u[e], rscale, gk, uk);
+    }
     bstore(k.out[0], voff, T::pack(y));
-    __builtin_amdgcn_sched_barrier(0);
+    order_fence();
 }
 
 // DR: accumulate go T_g T_u / (b1 b2) (/ b1 without linear beta) into acc;
@@ -132,17 +147,36 @@ __device__ __forceinline__ void bwd_chunk(const uint4 *v, const Chunk<3, 2> &k, 
     T::unpack(v[0], g);
     T::unpack(v[1], u);
     T::unpack(v[2], og);
+    // bf16 io with a linear beta: the polynomial up branch when the whole
+    // wavefront's |U| allows it.  Two half vectors, each with its own branch,
+    // keep the values live across a branch (and so the registers) halved.
+    const bool poly = LB && IO == IO_BF16 && wave_up_small<E>(u, uk);
+    const float cU4 = 0.25f * cU;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const BwdOut b = bwd_elem<LB, FAST, IO == IO_F32, !DR>(g[e], u[e], og[e], cG, cU, gk, uk);
-        dg[e] = b.dg;
-        du[e] = b.du;
-        if (DR)
-            acc += b.p;
+    for (int h = 0; h < E; h += E / 2) {
+        if (poly) {
+#pragma unroll
+            for (int e = h; e < h + E / 2; ++e) {
+                const BwdOut b = bwd_elem_small_u<FAST, !DR>(g[e], u[e], og[e], cG, cU4, gk, uk);
+                dg[e] = b.dg;
+                du[e] = b.du;
+                if (DR)
+                    acc += b.p;
+            }
+        } else {
+#pragma unroll
+            for (int e = h; e < h + E / 2; ++e) {
+                const BwdOut b = bwd_elem<LB, FAST, IO == IO_F32, !DR>(g[e], u[e], og[e], cG, cU, gk, uk);
+                dg[e] = b.dg;
+                du[e] = b.du;
+                if (DR)
+                    acc += b.p;
+            }
+        }
     }
     bstore(k.out[0], voff, T::pack(dg));
     bstore(k.out[1], voff, T::pack(du));
-    __builtin_amdgcn_sched_barrier(0);
+    order_fence();
 }
 
 // chunk index -> (row, chunk in row)
@@ -213,9 +247,15 @@ situ_glu_fwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ r
 #undef SITU_FWD_BODY
 }
 
+// Wavefronts per SIMD the backward kernels are built for (register budget
+// 512 / n): 8 for the plain math, 6 with a linear beta (the bf16 kernels
+// then carry both up-branch forms) or a bf16 routing weight, 5 with a
+// linear beta and a beta other than 4.
+#define SITU_BWD_MINW(LB, FAST, RWB) ((LB) && !(FAST) ? 5 : (LB) || (RWB) ? 6 : 8)
+
 // Backward without a routing-weight gradient, flat mapping.
 template <int IO, bool LB, bool FAST, bool RWB>
-__global__ void __launch_bounds__(256, LB || RWB ? 6 : 8)
+__global__ void __launch_bounds__(256, SITU_BWD_MINW(LB, FAST, RWB))
 situ_glu_bwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
                     uint32_t total, ChunkGeom g, GateK gk, UpK uk)
 {
@@ -252,7 +292,7 @@ situ_glu_bwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ r
 // row: d_rw[row]; one weight for all rows: the row's partial goes to
 // row_partials[row] for the fixed-order second pass.
 template <int IO, bool LB, bool FAST, bool RWB>
-__global__ void __launch_bounds__(1024, LB || RWB ? 6 : 8)
+__global__ void __launch_bounds__(1024, SITU_BWD_MINW(LB, FAST, RWB))
 situ_glu_bwd_dr_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride, const void *__restrict__ grad_out, void *__restrict__ d_gate_up,
                        void *__restrict__ d_rw, float *__restrict__ row_partials, int64_t rows, ChunkGeom g,
                        GateK gk, UpK uk)

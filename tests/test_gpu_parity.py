@@ -110,6 +110,37 @@ def test_small_workloads(name, rows, inter):
                   x["want_drw"], tag=f"{name}[{rows},{inter}]")
 
 
+@pytest.mark.parametrize("linear_beta", [25.0, 3.0, 0.5])
+@pytest.mark.parametrize("beta", [4.0, 2.5])
+def test_up_branch_polynomial_range(beta, linear_beta):
+    """bf16 io with a linear beta: a wavefront's chunk (512 values of a row)
+    whose |U| all lie within linear_beta / 4 takes the polynomial
+    tanh(U / linear_beta), a chunk with any |U| beyond takes the exponential
+    form.  U log-uniform over 1e-40 .. the bound with random signs, plus the
+    bound itself, zero, -0 and subnormals; in odd rows the first chunk also
+    holds the next bf16 value above the bound (that chunk takes the
+    exponential form, the second chunk the polynomial).  Every element
+    against the oracle, forward and backward with the routing-weight
+    gradient."""
+    rows, inter = 64, 1024
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    bound = 0.25 * linear_beta
+    mag = torch.exp(torch.empty(rows, inter).uniform_(math.log(1e-40), math.log(bound), generator=gen))
+    u = torch.where(torch.rand(rows, inter, generator=gen) < 0.5, -mag, mag)
+    u[:, 0], u[:, 1], u[:, 2], u[:, 3], u[:, 4] = bound, -bound, 0.0, -0.0, 3e-39
+    u[:, 512], u[:, 513] = bound, -bound
+    above = float((np.array([bound], dtype=np.float32).view(np.uint32) + (1 << 16)).view(np.float32)[0])
+    u[1::2, 5] = above
+    g = 2.0 * torch.randn(rows, inter, generator=gen)
+    gate_up = torch.cat([g, u], dim=1).to(torch.bfloat16)
+    assert float(gate_up[:, inter:].float().abs().max()) == above
+    assert float(gate_up[0, inter:].float().abs().max()) == bound
+    rw = torch.rand(rows, 1, generator=gen)
+    go = torch.randn(rows, inter, generator=gen).to(torch.bfloat16)
+    run_and_check(gate_up.to(DEV), rw.to(DEV), go.to(DEV), beta, linear_beta, True,
+                  tag=f"poly-range[b={beta},lb={linear_beta}]")
+
+
 def test_dense_ffn_broadcast_dr_small():
     """One broadcast weight with its gradient (sum over every row)."""
     x = inputs("dense_ffn", rows=20, inter=1000, seed=5)
