@@ -4,10 +4,12 @@ weighted SiTU-GLU parity bar:
   * bfloat16 outputs (Y, dG, dU): at most 1 ulp apart, measured as the
     ordinal distance between the GPU's bf16 value and the oracle's fp64 value
     rounded once to bf16 (round to nearest even); +0 and -0 are the same point.
-  * float32 outputs: |gpu - ref| <= 1e-5 |ref| for Y and dU.  For dG the
-    reference magnitude is the sum of the magnitudes of the two terms of
-    dT_g/dG (they cancel at the gate's minimum, where a relative bound on the
-    difference would measure only that cancellation).
+  * float32 outputs: |gpu - ref| <= 1e-5 |ref| for Y, dU and dG.  Where the
+    two terms of dT_g/dG cancel by a factor of at least 100 (near the gate's
+    minimum, where a relative bound on the difference would measure only that
+    cancellation), dG's reference magnitude is the sum of the magnitudes of
+    the two terms instead; the count of elements that pass only under that
+    relaxed scale is returned, so that the tests can report it.
   * dr: |gpu - ref| <= 1e-4 * sum_j |go T_g T_u| (the row sum's own condition
     scale), plus one ulp of the routing-weight dtype for its final rounding.
 
@@ -30,6 +32,7 @@ BF16_ULP_BAR = 1
 F32_REL = 1e-5
 DR_REL = 1e-4
 F32_MIN_NORMAL = 2.0 ** -126
+CANCEL_MIN = 100.0   # term-scale / |dG| from which dG's bar takes the term scale
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
@@ -87,18 +90,28 @@ def subnormal_allowance(gate_up64: np.ndarray, r64: np.ndarray, go64: np.ndarray
 
 def assert_f32_close(name: str, gpu: torch.Tensor, ref64: np.ndarray, scale64: np.ndarray | None = None,
                      rel: float = F32_REL, allow64: np.ndarray | None = None):
+    """fp32 parity.  Without scale64: the maximum relative error.  With
+    scale64 (dG's term scale): {"max_rel": ..., "relaxed": n}, n = elements
+    inside the bar only because their terms cancel by >= CANCEL_MIN."""
     g = gpu.detach().cpu().numpy().astype(np.float64).reshape(ref64.shape)
-    s = np.abs(ref64) if scale64 is None else np.maximum(np.abs(ref64), scale64)
-    s = np.maximum(s, F32_MIN_NORMAL)
+    plain = np.maximum(np.abs(ref64), F32_MIN_NORMAL)
+    s = plain
+    if scale64 is not None:
+        cancels = scale64 >= CANCEL_MIN * np.abs(ref64)
+        s = np.where(cancels, np.maximum(plain, scale64), plain)
     err = np.abs(g - ref64)
-    ok = err <= rel * s + (0.0 if allow64 is None else allow64)
+    extra = 0.0 if allow64 is None else allow64
+    ok = err <= rel * s + extra
     if not ok.all():
         i = tuple(np.argwhere(~ok)[0])
         raise AssertionError(
             f"{name}: {int((~ok).sum())} of {ok.size} fp32 elements outside {rel} relative; "
             f"first at {i}: gpu={g[i]!r} oracle={ref64[i]!r} scale={s[i]!r}")
     with np.errstate(divide="ignore", invalid="ignore"):
-        return float(np.nanmax(np.where(s > 0, err / s, 0.0))) if err.size else 0.0
+        max_rel = float(np.nanmax(np.where(s > 0, err / s, 0.0))) if err.size else 0.0
+    if scale64 is None:
+        return max_rel
+    return {"max_rel": max_rel, "relaxed": int(np.sum(err > rel * plain + extra))}
 
 
 def assert_dr_close(name: str, gpu: torch.Tensor, ref64: np.ndarray, abs_scale64: np.ndarray,

@@ -70,9 +70,9 @@ def worked_cases():
                 cur["beta2"] = None if rest == "none" else float(rest)
             elif key in ("G", "U", "go"):
                 cur[key] = [[parse_x(t) for t in row.split()] for row in rest.split(";")]
-            elif key in ("r", "dr"):
+            elif key in ("r", "dr", "dr_abs"):
                 cur[key] = [Fraction(t.strip()) for t in rest.split(";")]
-            else:  # Y, dG, dU: exact rationals per row
+            else:  # Y, dG, dU, dg_scale: exact rationals per row
                 cur[key] = [[Fraction(t) for t in row.split()] for row in rest.split(";")]
     return cases
 

@@ -70,16 +70,22 @@ def pin_worked_rows(lib):
         go = np.array(c["go"], dtype=np.float64)
         r = np.array([float(v) for v in c["r"]], dtype=np.float64)
         y = oracle.forward(gate_up, r, c["beta1"], c["beta2"], lib=lib)
-        b = oracle.backward(gate_up, r, go, c["beta1"], c["beta2"], want_dr=True, lib=lib)
+        b = oracle.backward(gate_up, r, go, c["beta1"], c["beta2"], want_dr=True, want_scales=True, lib=lib)
         inter = gate_up.shape[1] // 2
         for i in range(rows):
             for j in range(inter):
                 _close(y[i, j], c["Y"][i][j], 1e-12, 1e-13, f"{c['name']} Y[{i},{j}]")
                 _close(b["d_gate_up"][i, j], c["dG"][i][j], 1e-12, 1e-13, f"{c['name']} dG[{i},{j}]")
                 _close(b["d_gate_up"][i, inter + j], c["dU"][i][j], 1e-12, 1e-13, f"{c['name']} dU[{i},{j}]")
+                # the tolerance scales the parity bars rest on (dG's term scale)
+                _close(b["dg_scale"][i, j], c["dg_scale"][i][j], 1e-12, 1e-13, f"{c['name']} dg_scale[{i},{j}]")
         assert len(b["dr"]) == len(c["dr"]), c["name"]
         for i, v in enumerate(c["dr"]):
             _close(b["dr"][i], v, 1e-12, 1e-12, f"{c['name']} dr[{i}]")
+        # dr's condition scale, one per row
+        assert len(b["dr_abs"]) == len(c["dr_abs"]) == rows, c["name"]
+        for i, v in enumerate(c["dr_abs"]):
+            _close(b["dr_abs"][i], v, 1e-12, 1e-12, f"{c['name']} dr_abs[{i}]")
 
 
 # --------------------------------------------------------------------------

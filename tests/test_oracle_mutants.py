@@ -62,6 +62,15 @@ MUTANTS = {
         "dgu[inter + j] = o * r * tu * tgp;\n            dgu[j] = o * r * tg * tup;"),
     "dr_includes_r": ("double p = o * tg * tu;", "double p = o * r * tg * tu;"),
     "dr_uses_abs": ("acc += p;", "acc += fabs(p);"),
+    "dr_abs_includes_r": ("acc_abs += fabs(p);", "acc_abs += fabs(r * p);"),
+    "dr_abs_signed": ("acc_abs += fabs(p);", "acc_abs += p;"),
+    "dg_scale_drops_second_term": ("* (fabs(t1) + fabs(t2));", "* fabs(t1);"),
+    "dg_scale_signed_sum": ("* (fabs(t1) + fabs(t2));", "* fabs(t1 + t2);"),
+    "dg_scale_extra_beta": ("double t2 = beta1 * tanh(g / beta1) * s * sm;",
+                            "double t2 = beta1 * beta1 * tanh(g / beta1) * s * sm;"),
+    "dg_scale_without_r_and_tu": ("dg_scale[i * inter + j] = fabs(o * r * tu)", "dg_scale[i * inter + j] = fabs(o)"),
+    "dg_scale_sigmoid_not_mirrored": ("double s = logistic(g), sm = logistic(-g);",
+                                      "double s = logistic(g), sm = logistic(g);"),
     "bf16_truncates": ("double q = nearbyint(ax / quantum);", "double q = floor(ax / quantum);"),
     "bf16_ties_away": ("double q = nearbyint(ax / quantum);", "double q = round(ax / quantum);"),
     "bf16_no_subnormal_floor": ("    if (e < -126)\n        e = -126;", ""),
