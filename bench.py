@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the weighted SiTU-GLU hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload routed_top8]
+    python bench.py [--steps K] [--warmup W] [--workload dense_ffn]
 
 One step is one pass of the whole path over one batch: the forward kernel and
 the backward kernel (with d_routing_weights where the workload asks for it),
-inputs already resident in HBM.  The routed_top8_mxfp8 workload times the
+inputs already resident in HBM.  The default workload is the largest bf16
+forward + backward one, dense_ffn ([16384, 2 x 18432]); the routed and stress
+workloads are timed in the same run and summarised under other_workloads.  The routed_top8_mxfp8 workload times the
 forward with MXFP8 output instead (forward only); attn_res_mix times the
 attention-residual mixing kernel; grouped_fc1_top8 (bf16 operands) and
 grouped_fc1_top8_mxfp8 (MXFP8 operands) time the fused FC1 grouped GEMM +
 SiTU-GLU (value and roofline in TFLOP/s against the matrix-core peak of the
-operand type).  W untimed steps, then K timed steps between two device
+operand type).  The step first runs for --settle-ms (the GPU's clocks ramp
+up from idle), then W untimed steps, then K timed steps between two device
 synchronisations.  Prints ONE JSON line:
 
   value        whole-step algorithmic HBM throughput, GB/s (10^9 B/s): the bytes
@@ -20,8 +23,12 @@ synchronisations.  Prints ONE JSON line:
                (8 TB/s): algorithmic bytes per launch / its mean launch time,
                timed with HIP events on the stream it runs on around K
                back-to-back launches of that kernel
-  cpu_baseline the fp64 CPU oracle on a bounded sample of the same workload
-               (a reported baseline, not the target)
+  parity       the parity gate: the oracle on evenly spaced rows of the very
+               bytes the GPU read (copied back from HBM), against the timed
+               outputs at the parity bar; value is null when it fails
+  cpu_baseline the fp64 CPU oracle on those rows (a reported baseline, not
+               the target), and single-thread times of the two small
+               workloads
   cold_cache_and_ceilings
                (elementwise workloads) the median of each kernel's launches
                with a 512 MiB read before each one (nothing left in L2 or the
@@ -79,41 +86,147 @@ def _traffic(workload: str, kernel: str, source: str = KERNEL_SOURCE):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(workload: str, sample_rows: int) -> dict:
-    import numpy as np  # noqa: F401
-
-    import oracle
-    from ffn_gated_activation_amd.workloads import algorithmic_bytes, make_inputs
+def _cores() -> int:
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
-    x = make_inputs(workload, device="cpu", seed=0, rows=sample_rows)
-    gu = x["gate_up"].double().numpy()
-    rw = x["routing_weights"].double().numpy()
-    go = x["grad_out"].double().numpy() if x["grad_out"] is not None else None
-    mx = x["workload"].mx
+    return max(1, min(cores, 16))
+
+
+def _host_info() -> dict:
+    """The host and software the numbers were taken on."""
+    import platform
+
+    import torch
+    info = {"cpu_model": None, "host_threads": _cores(), "python": platform.python_version(),
+            "torch": torch.__version__, "hip_runtime": getattr(torch.version, "hip", None),
+            "rocm": None, "amdgpu_driver": None,
+            "gpu": torch.cuda.get_device_name(0) if torch.cuda.is_available() else None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    for key, path in (("rocm", "/opt/rocm/.info/version"), ("amdgpu_driver", "/sys/module/amdgpu/version")):
+        try:
+            with open(path) as f:
+                info[key] = f.read().strip()
+        except OSError:
+            pass
+    return info
+
+
+def _ordinal_bf16(bits):
+    import numpy as np
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _max_bf16_ulp(gpu, ref64) -> int:
+    """Largest ordinal distance between the GPU's bf16 values and the
+    oracle's fp64 values rounded once to bf16 (+0 and -0 the same point)."""
+    import numpy as np
+
+    import oracle
+    import torch
+    g = gpu.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(ref64.shape)
+    d = np.abs(_ordinal_bf16(g) - _ordinal_bf16(oracle.round_bf16_bits(ref64)))
+    return int(d.max()) if d.size else 0
+
+
+def _oracle_leg(name: str, x: dict, outs: dict, sample_elems: int, timed: bool) -> tuple:
+    """The oracle on rows of the very inputs the GPU ran on (copied back from
+    HBM): the parity gate (every output of those rows against the oracle at
+    the parity bar: 1 bf16 ulp; dr within 1e-4 of its row sum's condition
+    scale plus one ulp) and, when `timed`, the CPU baseline (the fp64 oracle's
+    forward and backward on those rows, on the host's cores)."""
+    import numpy as np
+
+    import oracle
+    import torch
+
+    from ffn_gated_activation_amd.workloads import algorithmic_bytes
+    gu, rw, go = x["gate_up"], x["routing_weights"], x["grad_out"]
+    rows, inter = gu.shape[0], gu.shape[1] // 2
+    n = max(1, min(rows, sample_elems // inter))
+    idx = torch.unique(torch.linspace(0, rows - 1, n, device=gu.device).round().long())
+    n = int(idx.numel())
+    broadcast = rw.numel() == 1 and rows != 1
+    want = x["want_drw"] and not broadcast
+    gu64 = gu.index_select(0, idx).double().cpu().numpy()
+    rw64 = (rw if broadcast else rw.index_select(0, idx)).double().cpu().numpy().reshape(-1)
+    go64 = None if go is None else go.index_select(0, idx).double().cpu().numpy()
+    cores = _cores()
     t0 = time.perf_counter()
-    y = oracle.forward(gu, rw, x["beta"], x["linear_beta"], threads=cores)
-    if mx:
-        oracle.mx_quantize(y, mx, "floor", threads=cores)
-    if go is not None:
-        bw = oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"],
-                             want_scales=False, threads=cores)
-        if mx:
-            inter = gu.shape[1] // 2
-            oracle.mx_quantize(bw["d_gate_up"][:, :inter], mx, "floor", threads=cores)
-            oracle.mx_quantize(bw["d_gate_up"][:, inter:], mx, "floor", threads=cores)
+    y = oracle.forward(gu64, rw64, x["beta"], x["linear_beta"], threads=cores)
+    b = None
+    if go64 is not None:
+        b = oracle.backward(gu64, rw64, go64, x["beta"], x["linear_beta"], want_dr=want, want_scales=want,
+                            threads=cores)
     dt = time.perf_counter() - t0
-    b = algorithmic_bytes(workload, rows=sample_rows)["total"]
-    what = ("fp64 forward+backward + MXFP8 quantisation of Y, dG and dU" if mx and go is not None else
-            "fp64 forward + MXFP8 quantisation" if mx else
-            "fp64 forward+backward" if go is not None else "fp64 forward")
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{workload} recipe, first {sample_rows} rows (seed 0, drawn on the host), "
-                      f"{what}, {dt:.2f} s wall",
-            "rows_per_s": round(sample_rows / dt, 1)}
+    if "y" not in outs or gu.dtype != torch.bfloat16:
+        parity = None        # MXFP8 or fp32 outputs: the GPU tests check those against the oracle
+    else:
+        parity = _parity(outs, idx, inter, y, b, want, n, rows)
+    base = None
+    if timed:
+        nbytes = algorithmic_bytes(name, rows=n)["total"]
+        what = "fp64 forward+backward" if go is not None else "fp64 forward"
+        base = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{name}: {n} of its {rows} rows, evenly spaced, the same bytes the GPU read "
+                          f"(copied back from HBM), {what}, {dt:.2f} s wall",
+                "rows_per_s": round(n / dt, 1)}
+    return base, parity
+
+
+def _parity(outs: dict, idx, inter: int, y, b, want: bool, n: int, rows: int) -> dict:
+    """bf16 outputs of the sampled rows against the oracle: at most 1 ulp;
+    dr within 1e-4 of its row sum's condition scale plus one fp32 ulp."""
+    import numpy as np
+    parity = {"rows_checked": n, "of_rows": rows, "values_checked": n * inter * (1 if b is None else 3),
+              "max_bf16_ulp": {"y": _max_bf16_ulp(outs["y"].index_select(0, idx), y)}}
+    if b is not None:
+        d = outs["dgu"].index_select(0, idx)
+        parity["max_bf16_ulp"]["dG"] = _max_bf16_ulp(d[:, :inter], b["d_gate_up"][:, :inter])
+        parity["max_bf16_ulp"]["dU"] = _max_bf16_ulp(d[:, inter:], b["d_gate_up"][:, inter:])
+        if want:
+            g = outs["drw"].index_select(0, idx).double().cpu().numpy().reshape(-1)
+            err = np.abs(g - b["dr"])
+            tol = 1e-4 * np.maximum(b["dr_abs"], 2.0 ** -126) + 2.0 ** -24 * np.abs(b["dr"])
+            parity["dr_max_err_over_scale"] = float(np.max(err / np.maximum(b["dr_abs"], 1e-300)))
+            parity["dr_within_bar"] = bool(np.all(err <= tol))
+    parity["pass"] = max(parity["max_bf16_ulp"].values()) <= 1 and parity.get("dr_within_bar", True)
+    return parity
+
+
+def _single_thread_oracle() -> dict:
+    """The oracle on one host thread at the two small workloads: all of
+    fp32_small (forward + backward + dr) and all of top1_fwd (forward)."""
+    import oracle
+
+    from ffn_gated_activation_amd.workloads import algorithmic_bytes, make_inputs
+    out = {}
+    for name in ("fp32_small", "top1_fwd"):
+        x = make_inputs(name, device="cpu", seed=0)
+        gu = x["gate_up"].double().numpy()
+        rw = x["routing_weights"].double().numpy().reshape(-1)
+        go = None if x["grad_out"] is None else x["grad_out"].double().numpy()
+        t0 = time.perf_counter()
+        oracle.forward(gu, rw, x["beta"], x["linear_beta"], threads=1)
+        if go is not None:
+            oracle.backward(gu, rw, go, x["beta"], x["linear_beta"], want_dr=x["want_drw"], want_scales=False,
+                            threads=1)
+        dt = time.perf_counter() - t0
+        rows = gu.shape[0]
+        out[name] = {"rows": rows, "seconds": round(dt, 4), "rows_per_s": round(rows / dt, 1),
+                     "GB/s": round(algorithmic_bytes(name)["total"] / dt / 1e9, 4),
+                     "passes": "fwd+bwd+dr" if go is not None else "fwd", "threads": 1,
+                     "inputs": "drawn on the host (seed 0)"}
+    return out
 
 
 def _copy_calibration(args, dev):
@@ -162,6 +275,7 @@ def bench_attn_res(args) -> int:
     def step():
         situ_glu_attn_res_fwd(x["blocks"], x["prefix"], x["norm_weight"], x["proj_weight"], w.eps, out=out)
 
+    settle_ms = _settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -191,6 +305,8 @@ def bench_attn_res(args) -> int:
                    "hidden": w.hidden, "eps": w.eps, "algorithmic_bytes_per_step": nbytes},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
+        "clock_settle_ms": round(settle_ms, 1),
+        "host": _host_info(),
         "kernels": {"attn_res": {"ms": round(k_ms, 5), "bytes": nbytes, "GB/s": round(achieved, 2)}},
         "roofline": {"bound": "hbm", "kernel": "situ_glu_attn_res_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -371,6 +487,7 @@ def bench_grouped(args) -> int:
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / n
 
+    settle_ms = _settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -439,6 +556,8 @@ def bench_grouped(args) -> int:
                    "flops_per_step": flops},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "rows_per_s": round(w.rows / (ms / 1e3), 1),
+        "clock_settle_ms": round(settle_ms, 1),
+        "host": _host_info(),
         "kernels": kernels,
         "roofline": {"bound": "mfma",
                      "kernel": ("situ_glu_grouped_fwd_kernel, with the two situ_mx_scales_stage_major_kernel "
@@ -453,89 +572,71 @@ def bench_grouped(args) -> int:
     return 0
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    # the GPU's clocks take ~50 steps (~25 ms) to settle from idle; 200 warm-up
-    # steps keep that ramp out of the timed region
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="routed_top8")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=65536,
-                    help="rows of the CPU-oracle sample (capped at the workload's rows)")
-    ap.add_argument("--cpu-sample-rows-gemm", type=int, default=65536,
-                    help="rows of the CPU-oracle sample of the grouped GEMM workload")
-    ap.add_argument("--compare-unfused", action="store_true",
-                    help="grouped GEMM workloads: also time the library GEMM (torch._grouped_mm for bf16, "
-                         "torch._scaled_mm with MX scales on the same FLOPs for MXFP8) + the activation kernel "
-                         "(context)")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache medians and the plain-kernel ceilings")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter calibration runs)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the weighted SiTU-GLU path is row parallel and is measured "
-              "on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
-        return 2
-
+def _settle(fn, ms: float) -> float:
+    """Run fn back to back for at least `ms` milliseconds of wall time (the
+    GPU's clocks ramp up from idle over the first ~25 ms of load); returns
+    the milliseconds spent."""
     import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
 
-    from ffn_gated_activation_amd.workloads import ATTN_RES, GROUPED, GROUPED_MX
-    if args.workload in ATTN_RES or args.workload in GROUPED or args.workload in GROUPED_MX:
-        if not torch.cuda.is_available():
-            print("bench.py needs a GPU", file=sys.stderr)
-            return 2
-        return bench_attn_res(args) if args.workload in ATTN_RES else bench_grouped(args)
+
+def _elementwise(name: str, args, dev, full: bool) -> tuple:
+    """Time one elementwise workload: clock settle, W warm-up steps, K timed
+    steps between synchronisations (wall clock), then each kernel alone, K
+    back-to-back launches between two HIP events on its stream.  With
+    `full`, also the cold-cache medians and plain-kernel ceilings.  Returns
+    (record, inputs, outputs)."""
+    import torch
 
     from ffn_gated_activation_amd import situ_glu_bwd, situ_glu_bwd_mxfp8, situ_glu_fwd, situ_glu_fwd_mxfp8
     from ffn_gated_activation_amd.workloads import WORKLOADS, algorithmic_bytes, make_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    w = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    x = make_inputs(args.workload, device=dev, seed=0)
+    w = WORKLOADS[name]
+    x = make_inputs(name, device=dev, seed=0)
     gu, rw, go = x["gate_up"], x["routing_weights"], x["grad_out"]
     beta, lb, want = x["beta"], x["linear_beta"], x["want_drw"]
+    outs = {}
     if w.mx:
         codes = torch.empty(w.rows, w.inter, dtype=torch.uint8, device=dev)
         scales = torch.empty(w.rows, -(-w.inter // 32), dtype=torch.uint8, device=dev)
     else:
-        y = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
-    dgu = torch.empty_like(gu) if w.backward and not w.mx else None
+        outs["y"] = torch.empty(w.rows, w.inter, dtype=w.dtype, device=dev)
+    if w.backward and not w.mx:
+        outs["dgu"] = torch.empty_like(gu)
     if w.backward and w.mx:
         dcodes = torch.empty(w.rows, 2 * w.inter, dtype=torch.uint8, device=dev)
         dscales = torch.empty(w.rows, 2 * -(-w.inter // 32), dtype=torch.uint8, device=dev)
-    drw = torch.empty_like(rw) if want else None
+    if want:
+        outs["drw"] = torch.empty_like(rw)
     torch.cuda.synchronize()
 
     def fwd():
         if w.mx:
             situ_glu_fwd_mxfp8(gu, rw, beta, lb, w.mx, "floor", codes=codes, scales=scales)
         else:
-            situ_glu_fwd(gu, rw, beta, lb, out=y)
+            situ_glu_fwd(gu, rw, beta, lb, out=outs["y"])
 
     def bwd():
         if w.mx:
             situ_glu_bwd_mxfp8(gu, rw, go, beta, lb, want, w.mx, "floor", d_codes=dcodes, d_scales=dscales,
-                               d_routing_weights=drw)
+                               d_routing_weights=outs.get("drw"))
         else:
-            situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgu, d_routing_weights=drw)
+            situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=outs["dgu"],
+                         d_routing_weights=outs.get("drw"))
 
     def step():
         fwd()
         if w.backward:
             bwd()
 
+    settle_ms = _settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
     # timed region: K steps between synchronisations (wall clock) ...
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -559,7 +660,7 @@ def main(argv=None) -> int:
     bwd_ms = ev[1].elapsed_time(ev[2]) / args.steps if w.backward else 0.0
 
     unfused = {}
-    if w.mx:
+    if w.mx and full:
         # context: the bf16 kernels followed by the stand-alone MXFP8 quantiser (same blocks and rounding;
         # with I a multiple of 32 one quantiser call over [rows, 2I] gives d_gate_up's layout)
         from ffn_gated_activation_amd import situ_glu_mx_quantize
@@ -574,10 +675,10 @@ def main(argv=None) -> int:
             dgb = torch.empty_like(gu)
 
             def bwd_unfused():
-                situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgb, d_routing_weights=drw)
+                situ_glu_bwd(gu, rw, go, beta, lb, want_drw=want, d_gate_up=dgb, d_routing_weights=outs.get("drw"))
                 situ_glu_mx_quantize(dgb, w.mx, "floor", codes=dcodes, scales=dscales)
             fns["unfused_bwd_then_quantize"] = bwd_unfused
-        for name, fn in fns.items():
+        for uname, fn in fns.items():
             for _ in range(5):
                 fn()
             torch.cuda.synchronize()
@@ -586,37 +687,28 @@ def main(argv=None) -> int:
                 fn()
             ev2[1].record()
             torch.cuda.synchronize()
-            unfused[name] = {"ms": round(ev2[0].elapsed_time(ev2[1]) / args.steps, 5)}
+            unfused[uname] = {"ms": round(ev2[0].elapsed_time(ev2[1]) / args.steps, 5)}
 
-    _copy_calibration(args, dev)
-
-    ab = algorithmic_bytes(args.workload)
+    if full:
+        _copy_calibration(args, dev)
+    ab = algorithmic_bytes(name)
     cold = None
-    if not args.no_cold:
+    if full and not args.no_cold:
         ks = {"fwd": fwd, "bwd": bwd} if w.backward else {"fwd": fwd}
         cold = _cold_and_ceilings(ks, ab, w.rows, w.inter, min(args.steps, 20), dev)
     ms_per_step = wall / args.steps * 1e3
     value = ab["total"] / (ms_per_step / 1e3) / 1e9
     dom = "bwd" if w.backward else "fwd"
-    dom_bytes = ab[dom]
     dom_ms = bwd_ms if w.backward else fwd_ms
-    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    kname = ("situ_glu_bwd_mx_kernel" if w.backward and w.mx else "situ_glu_bwd_kernel" if w.backward else
+    achieved = ab[dom] / (dom_ms / 1e3) / 1e9
+    kname = ("situ_glu_bwd_mx_kernel" if w.backward and w.mx else
+             ("situ_glu_bwd_dr_kernel" if want else "situ_glu_bwd_kernel") if w.backward else
              "situ_glu_fwd_mx_kernel" if w.mx else "situ_glu_fwd_kernel")
     src = MX_KERNEL_SOURCE if w.mx else KERNEL_SOURCE
     rec = {
-        "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rows": w.rows,
                    "intermediate": w.inter, "beta": w.beta, "linear_beta": w.linear_beta,
                    "passes": ("fwd+bwd" + ("+d_routing_weights" if want else "") +
@@ -625,6 +717,7 @@ def main(argv=None) -> int:
                    "algorithmic_bytes_per_step": ab["total"]},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "rows_per_s": round(w.rows / (ms_per_step / 1e3), 1),
+        "clock_settle_ms": round(settle_ms, 1),
         "kernels": {
             "fwd": {"ms": round(fwd_ms, 5), "bytes": ab["fwd"],
                     "GB/s": round(ab["fwd"] / (fwd_ms / 1e3) / 1e9, 2)},
@@ -634,13 +727,110 @@ def main(argv=None) -> int:
         },
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic(args.workload, dom, src)},
+                     "traffic": _traffic(name, dom, src)},
         "cold_cache_and_ceilings": cold,
-        "cpu_baseline": None,
     }
+    return rec, x, outs
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
+    # the GPU's clocks take ~25 ms of load to ramp up from idle: the step runs
+    # for this long before the warm-up steps, whatever --warmup is
+    ap.add_argument("--settle-ms", type=float, default=100.0)
+    ap.add_argument("--workload", default="dense_ffn")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated elementwise workloads also timed in the same run and summarised under "
+                         "'other_workloads' (default for dense_ffn: routed_top8,stress_sat; '' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg: the CPU baseline and the parity gate on the same bytes")
+    ap.add_argument("--cpu-sample-elems", type=int, default=3 << 26,
+                    help="values per half row times rows of the oracle sample (rows evenly spaced)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=65536,
+                    help="attention-residual and grouped GEMM workloads: rows of the CPU-oracle sample")
+    ap.add_argument("--cpu-sample-rows-gemm", type=int, default=65536,
+                    help="rows of the CPU-oracle sample of the grouped GEMM workload")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="grouped GEMM workloads: also time the library GEMM (torch._grouped_mm for bf16, "
+                         "torch._scaled_mm with MX scales on the same FLOPs for MXFP8) + the activation kernel "
+                         "(context)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache medians and the plain-kernel ceilings")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the weighted SiTU-GLU path is row parallel and is measured "
+              "on a single MI355X; --gpus above 1 is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from ffn_gated_activation_amd.workloads import ATTN_RES, GROUPED, GROUPED_MX, WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.workload in ATTN_RES or args.workload in GROUPED or args.workload in GROUPED_MX:
+        return bench_attn_res(args) if args.workload in ATTN_RES else bench_grouped(args)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    rec, x, outs = _elementwise(args.workload, args, dev, full=True)
+    parity = cpu = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = _cpu_baseline(args.workload, min(args.cpu_sample_rows, w.rows))
-    print(json.dumps(rec), flush=True)
+        cpu, parity = _oracle_leg(args.workload, x, outs, args.cpu_sample_elems, timed=True)
+        cpu["single_thread"] = _single_thread_oracle()
+    del x, outs
+    torch.cuda.empty_cache()
+    also = args.also
+    if also is None:
+        also = "routed_top8,stress_sat" if args.workload == "dense_ffn" else ""
+    others = {}
+    for name in [n for n in also.split(",") if n]:
+        r, xo, oo = _elementwise(name, args, dev, full=False)
+        par = None if args.no_cpu_baseline else _oracle_leg(name, xo, oo, 1 << 22, timed=False)[1]
+        others[name] = {"GB/s": r["value"], "pct_of_hbm_peak": r["pct_of_hbm_peak"],
+                        "ms_per_step": r["ms_per_step"], "rows_per_s": r["rows_per_s"],
+                        "kernels": r["kernels"], "roofline_frac": r["roofline"]["frac"],
+                        "roofline_kernel": r["roofline"]["kernel"], "parity": par}
+        if par is not None and not par["pass"]:
+            others[name]["GB/s"] = None
+        del xo, oo
+        torch.cuda.empty_cache()
+    value = rec["value"]
+    if parity is not None and parity.get("pass") is False:
+        value = None    # a step whose outputs disagree with the oracle reports no throughput
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": rec["dtype"],
+        "data": "synthetic",
+        "config": rec["config"],
+        "pct_of_hbm_peak": rec["pct_of_hbm_peak"],
+        "rows_per_s": rec["rows_per_s"],
+        "clock_settle_ms": rec["clock_settle_ms"],
+        "parity": parity,
+        "kernels": rec["kernels"],
+        "roofline": rec["roofline"],
+        "cold_cache_and_ceilings": rec["cold_cache_and_ceilings"],
+        "other_workloads": others or None,
+        "host": _host_info(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
     return 0
 
 
