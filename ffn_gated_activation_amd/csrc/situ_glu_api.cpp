@@ -109,7 +109,7 @@ namespace situ {
 namespace {
 
 // Truncated Taylor series c[k] = f^(k)(x0)/k! in long double.
-constexpr int kJ = 6;
+constexpr int kJ = 10;
 struct Jet {
     long double c[kJ];
 };
@@ -243,11 +243,17 @@ GateK make_gate_consts(double beta1)
     k.c1 = (float)s.c[1];
     k.c2 = (float)s.c[2];
     k.c3 = (float)s.c[3];
-    // Half width: at most 1/64 and |G*|/4 (so that G - G*_f32 is exact), and
-    // small enough that the dropped quartic term stays below 3e-7 of the
-    // linear one: |c4/c1| hw^3 <= 3e-7 (the higher terms add less than that).
-    long double hw = 1.0L / 64.0L;
-    const long double q = fabsl(s.c[4]) > 0 ? cbrtl(3e-7L * fabsl(s.c[1] / s.c[4])) : hw;
+    k.c4 = (float)s.c[4];
+    k.c5 = (float)s.c[5];
+    k.c6 = (float)s.c[6];
+    k.c7 = (float)s.c[7];
+    // Half width: at most 1/8 and |G*|/4 (so that G - G*_f32 is exact), and
+    // small enough that the dropped eighth-order term stays below 3e-7 of the
+    // linear one: |c8/c1| hw^7 <= 3e-7 (the higher terms add less than that).
+    // Outside it the terms of the plain difference cancel by a factor of
+    // about 16 or less, so its fp32 rounding stays near 5e-6.
+    long double hw = 1.0L / 8.0L;
+    const long double q = fabsl(s.c[8]) > 0 ? powl(3e-7L * fabsl(s.c[1] / s.c[8]), 1.0L / 7.0L) : hw;
     if (q < hw)
         hw = q;
     if (fabsl(gstar) / 4.0L < hw)
@@ -387,8 +393,8 @@ size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate, int64_t 
 }
 
 // Exposed for tests: the root-window constants the kernels use for a beta:
-// out[0] = G*_f32, out[1] = cubic half width, out[2..5] = c0..c3,
-// out[6] = the bf16 value nearest G*, out[7] = dT_g/dG there.
+// out[0] = G*_f32, out[1] = half width, out[2..9] = c0..c7,
+// out[10] = the bf16 value nearest G*, out[11] = dT_g/dG there.
 int situ_glu_gate_window(double beta, float *out)
 {
     g_last_error.clear();
@@ -403,8 +409,12 @@ int situ_glu_gate_window(double beta, float *out)
     out[3] = k.c1;
     out[4] = k.c2;
     out[5] = k.c3;
-    out[6] = k.gsub;
-    out[7] = 4.0f * k.tsub;
+    out[6] = k.c4;
+    out[7] = k.c5;
+    out[8] = k.c6;
+    out[9] = k.c7;
+    out[10] = k.gsub;
+    out[11] = 4.0f * k.tsub;
     return SITU_OK;
 }
 

@@ -220,7 +220,8 @@ __device__ __forceinline__ float fwd_elem_small_u(float g, float u, float rscale
 }
 
 // dT_g/dG / 4 near its root, where its two terms cancel.  fp32 io: the
-// cubic in d = G - G*_f32 inside the window.  bf16 io: G is a bf16 value, and
+// degree-7 Taylor polynomial in d = G - G*_f32 inside the window.  bf16 io: G
+// is a bf16 value, and
 // only the one nearest the root loses more than ~3e-5 to the cancellation;
 // that value gets its exact dT_g/dG / 4.  `plain` elsewhere.
 template <bool PRECISE>
@@ -228,7 +229,14 @@ __device__ __forceinline__ float gate_grad4_window(float g, float plain, const G
 {
     if (PRECISE) {
         const float d = g - k.win_ghi;  // exact (Sterbenz) inside the window
-        const float p = fmaf(fmaf(fmaf(0.25f * k.c3, d, 0.25f * k.c2), d, 0.25f * k.c1), d, 0.25f * k.c0);
+        float p = 0.25f * k.c7;
+        p = fmaf(p, d, 0.25f * k.c6);
+        p = fmaf(p, d, 0.25f * k.c5);
+        p = fmaf(p, d, 0.25f * k.c4);
+        p = fmaf(p, d, 0.25f * k.c3);
+        p = fmaf(p, d, 0.25f * k.c2);
+        p = fmaf(p, d, 0.25f * k.c1);
+        p = fmaf(p, d, 0.25f * k.c0);
         return fabsf(d) <= k.win_hw ? p : plain;
     } else {
         return g == k.gsub ? k.tsub : plain;

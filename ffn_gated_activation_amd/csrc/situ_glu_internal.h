@@ -12,7 +12,7 @@ namespace situ {
 //   y1 = 2|G|/b1       = |G| * y1k    (argument of 1 - e1 = 1 - exp(-y1))
 // The root window: dT_g/dG vanishes at G* < 0, where its two terms cancel.
 // Inside |G - win_ghi| <= win_hw the fp32-io kernels evaluate dT_g/dG as the
-// cubic c0 + c1 d + c2 d^2 + c3 d^3 in d = G - win_ghi (the Taylor expansion
+// degree-7 polynomial c0 + c1 d + ... + c7 d^7 in d = G - win_ghi (the Taylor expansion
 // at the fp32 number nearest G*) instead of the cancelling difference; the
 // bf16-io kernels, whose inputs are bf16 values, replace dT_g/dG / 4 at the
 // one bf16 value nearest G* (gsub) by its exact value (tsub); at every
@@ -24,7 +24,7 @@ struct GateK {
     float y1k;
     float win_ghi;
     float win_hw;
-    float c0, c1, c2, c3;
+    float c0, c1, c2, c3, c4, c5, c6, c7;
     float gsub, tsub;
 };
 

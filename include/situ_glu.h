@@ -431,11 +431,11 @@ int situ_glu_abi_version(void);
  * dT_g/dG cancel (Megatron-LM PR "Add SiTU-GLU through Transformer Engine",
  * section "Activation": T_g has its minimum at G*), so inside
  * |G - out[0]| <= out[1] the fp32-io kernels evaluate dT_g/dG as
- * out[2] + out[3] d + out[4] d^2 + out[5] d^3 with d = G - out[0]
+ * out[2] + out[3] d + out[4] d^2 + ... + out[9] d^7 with d = G - out[0]
  * (out[0] = G* rounded to fp32).  The bf16-io kernels, whose inputs are bf16
- * values, take dT_g/dG = out[7] at the one bf16 input G = out[6] nearest G*
- * (the only bf16 value where the cancellation costs more than ~3e-5 relative)
- * and the plain formula elsewhere.  out must hold 8 floats.
+ * values, take dT_g/dG = out[11] at the one bf16 input G = out[10] nearest
+ * G* (the only bf16 value where the cancellation costs more than ~3e-5
+ * relative) and the plain formula elsewhere.  out must hold 12 floats.
  * Returns SITU_OK or SITU_ERR_INVALID_ARG (bad beta, NULL out).
  */
 int situ_glu_gate_window(double beta, float *out);
