@@ -28,6 +28,7 @@ SITU_MX_BLOCK = 32
 SITU_GROUPED_MAX_EXPERTS = 4096
 SITU_GROUPED_MAX_HIDDEN = 1 << 20
 SITU_GROUPED_MAX_INTERMEDIATE = 1 << 20
+SITU_NOALLOC_MAX_ROWS = 262144
 ABI_VERSION = 8
 
 # every symbol include/situ_glu.h declares
@@ -35,7 +36,8 @@ EXPORTED = ("situ_glu_fwd", "situ_glu_bwd", "situ_glu_bwd_workspace_bytes",
             "situ_glu_last_error", "situ_glu_abi_version", "situ_glu_gate_window",
             "situ_glu_fwd_mxfp8", "situ_glu_mx_quantize", "situ_glu_attn_res_fwd",
             "situ_glu_grouped_fwd", "situ_glu_grouped_fwd_mxfp8",
-            "situ_glu_grouped_fwd_mxfp8_workspace_bytes", "situ_glu_bwd_mxfp8", "situ_glu_split")
+            "situ_glu_grouped_fwd_mxfp8_workspace_bytes", "situ_glu_bwd_mxfp8", "situ_glu_split",
+            "situ_glu_bwd_noalloc")
 
 
 class SituGluError(RuntimeError):
@@ -55,6 +57,8 @@ def _bind(lib):
     lib.situ_glu_bwd.restype = i32
     lib.situ_glu_bwd.argtypes = [vp, i32, i64, i64, vp, i32, i64, dbl, dblp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    lib.situ_glu_bwd_noalloc.restype = i32
+    lib.situ_glu_bwd_noalloc.argtypes = [vp, i32, i64, i64, vp, i32, i64, dbl, dblp, vp, vp, vp, vp]
     lib.situ_glu_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.situ_glu_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.situ_glu_last_error.restype = ctypes.c_char_p

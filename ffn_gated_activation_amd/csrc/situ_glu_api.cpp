@@ -496,10 +496,16 @@ int situ_glu_fwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     return SITU_OK;
 }
 
-int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
-                 const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
-                 const double *linear_beta, const void *grad_out, void *d_gate_up,
-                 void *d_routing_weights, void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// situ_glu_bwd, with the broadcast-dr workspace either the caller's or (own_scratch) the
+// library's per-device scratch array.
+int bwd_entry(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate, const void *routing_weights,
+              int rw_dtype, int64_t rw_rows, double beta, const double *linear_beta, const void *grad_out,
+              void *d_gate_up, void *d_routing_weights, void *workspace, size_t workspace_bytes, bool own_scratch,
+              void *stream)
 {
     g_last_error.clear();
     int rc = check_common(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows,
@@ -529,7 +535,18 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
         return fail(SITU_ERR_INVALID_ARG, "d_gate_up is not aligned to its element size");
     const bool broadcast_dr = d_routing_weights && rw_rows == 1 && rows > 1;
     const size_t need = broadcast_dr ? (size_t)rows * sizeof(float) : 0;
-    if (need) {
+    if (need && own_scratch) {
+        if (rows > SITU_NOALLOC_MAX_ROWS)
+            return fail(SITU_ERR_UNSUPPORTED,
+                        "one broadcast routing weight with its gradient needs %lld rows of scratch; the "
+                        "library's scratch holds %d (SITU_NOALLOC_MAX_ROWS)", (long long)rows,
+                        (int)SITU_NOALLOC_MAX_ROWS);
+        int err = 0;
+        workspace = situ::device_scratch(&err);
+        if (!workspace)
+            return fail(SITU_ERR_DEVICE, "scratch address lookup failed: %s", situ::device_error_string(err));
+        workspace_bytes = (size_t)SITU_NOALLOC_MAX_ROWS * sizeof(float);
+    } else if (need) {
         if (!workspace)
             return fail(SITU_ERR_INVALID_ARG, "workspace is NULL but %zu bytes are needed", need);
         if (workspace_bytes < need)
@@ -542,7 +559,8 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     const Range in_go = range("grad_out", grad_out, rows * intermediate * es);
     const Range o_dgu = range("d_gate_up", d_gate_up, rows * intermediate * 2 * es);
     const Range o_drw = range("d_routing_weights", d_routing_weights, d_routing_weights ? rw_rows * rs : 0);
-    const Range o_ws = range("workspace", workspace, (int64_t)need);
+    // the library's own scratch is a separate allocation: it overlaps no caller buffer
+    const Range o_ws = range("workspace", workspace, own_scratch ? 0 : (int64_t)need);
     const Range ins[] = {in_gu, in_rw, in_go};
     const Range outs[] = {o_dgu, o_drw, o_ws};
     for (const Range &o : outs)
@@ -576,6 +594,28 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t interm
     if (err)
         return fail(SITU_ERR_DEVICE, "backward launch failed: %s", situ::device_error_string(err));
     return SITU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                 const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                 const double *linear_beta, const void *grad_out, void *d_gate_up,
+                 void *d_routing_weights, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return bwd_entry(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows, beta, linear_beta,
+                     grad_out, d_gate_up, d_routing_weights, workspace, workspace_bytes, false, stream);
+}
+
+int situ_glu_bwd_noalloc(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,
+                         const void *routing_weights, int rw_dtype, int64_t rw_rows, double beta,
+                         const double *linear_beta, const void *grad_out, void *d_gate_up,
+                         void *d_routing_weights, void *stream)
+{
+    return bwd_entry(gate_up, io_dtype, rows, intermediate, routing_weights, rw_dtype, rw_rows, beta, linear_beta,
+                     grad_out, d_gate_up, d_routing_weights, nullptr, 0, true, stream);
 }
 
 int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t intermediate,

@@ -241,6 +241,11 @@ int launch_mx_quant(const MxQuantLaunch &L, void *stream);
 int launch_dr_reduce(const float *row_partials, int64_t rows, void *d_rw, int rw_bf16, void *stream);
 int launch_attn_res(const AresLaunch &L, void *stream);
 int launch_grouped_fwd(const GroupedLaunch &L, void *stream);
+// The library's per-device scratch array (a file-scope __device__ array of
+// SITU_NOALLOC_MAX_ROWS floats in situ_glu_kernels.hip): its device address
+// on the current device, looked up once per device; NULL with *err set to the
+// hipError_t when the lookup fails.
+float *device_scratch(int *err);
 // Zero `bytes` bytes at device pointer p with a fill kernel.
 int launch_zero(void *p, int64_t bytes, void *stream);
 const char *device_error_string(int err);

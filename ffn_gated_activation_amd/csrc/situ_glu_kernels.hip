@@ -28,6 +28,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "situ_glu.h"
 #include "situ_glu_device.h"
 #include "situ_glu_internal.h"
 
@@ -521,5 +524,40 @@ int launch_zero(void *p, int64_t bytes, void *stream)
 }
 
 const char *device_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+// ---------------------------------------------------------------- scratch of the allocation-free backward
+//
+// Every device the library runs on holds one copy of this array until the
+// process ends.  Host code never uses its name as an address: the name is a
+// host-side stand-in.  Its device address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) float scratch[SITU_NOALLOC_MAX_ROWS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+float *device_scratch(int *err)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    return g_scratch_ptr[dev];
+}
 
 }  // namespace situ

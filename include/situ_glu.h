@@ -150,6 +150,34 @@ int situ_glu_bwd(const void *gate_up, int io_dtype, int64_t rows,
 size_t situ_glu_bwd_workspace_bytes(int64_t rows, int64_t intermediate,
                                     int64_t rw_rows);
 
+/* Rows of the library's own scratch array (situ_glu_bwd_noalloc). */
+#define SITU_NOALLOC_MAX_ROWS 262144
+
+/*
+ * situ_glu_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under stream capture into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, layout, results and errors as situ_glu_bwd; where situ_glu_bwd
+ * would need a workspace (one routing weight broadcast over rows > 1 rows,
+ * with d_routing_weights), the per-row partials go to a scratch array the
+ * library holds on every device it runs on (SITU_NOALLOC_MAX_ROWS floats,
+ * 1 MiB, kept until the process ends), and more rows than that are
+ * SITU_ERR_UNSUPPORTED (nothing is launched).  The call allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library routine); the first call
+ * on a device looks the scratch array's address up once.
+ * Every call on one GPU shares that GPU's scratch array: two calls that may
+ * run at the same time on one GPU (different streams, no ordering between
+ * them) race on it, and their routing-weight gradients are then undefined.
+ * Every partial it reads was written by the same call, so nothing needs
+ * clearing between calls.
+ */
+int situ_glu_bwd_noalloc(const void *gate_up, int io_dtype, int64_t rows,
+                         int64_t intermediate, const void *routing_weights,
+                         int rw_dtype, int64_t rw_rows, double beta,
+                         const double *linear_beta, const void *grad_out,
+                         void *d_gate_up, void *d_routing_weights,
+                         void *stream);
+
 /*
  * Forward with MXFP8 output: Y = r * T_g(G) * T_u(U) as in situ_glu_fwd,
  * written as MXFP8 blocks instead of io_dtype values.  The Megatron-LM PR

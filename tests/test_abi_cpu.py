@@ -107,6 +107,39 @@ def test_bwd_rejects(lib, capi, kw):
     assert capi.last_error(lib) != ""
 
 
+def _bwd_noalloc(lib, **kw):
+    a = dict(gate_up=FAKE, io=1, rows=4, inter=8, rw=FAKE + 4096, rwd=0, rw_rows=4, beta=4.0, lb=25.0,
+             go=FAKE + 8192, dgu=FAKE + 16384, drw=FAKE + 32768)
+    a.update(kw)
+    lb = None if a["lb"] is None else ctypes.pointer(ctypes.c_double(a["lb"]))
+    return lib.situ_glu_bwd_noalloc(a["gate_up"], a["io"], a["rows"], a["inter"], a["rw"], a["rwd"],
+                                    a["rw_rows"], a["beta"], lb, a["go"], a["dgu"], a["drw"], None)
+
+
+BAD_BWD_NOALLOC = [k for k in BAD_BWD if "ws" not in k and k != dict(rw_rows=1)]
+
+
+@pytest.mark.parametrize("kw", BAD_BWD_NOALLOC, ids=[str(k) for k in BAD_BWD_NOALLOC])
+def test_bwd_noalloc_rejects(lib, capi, kw):
+    """The allocation-free backward validates its arguments as situ_glu_bwd
+    does, before any device work."""
+    rc = _bwd_noalloc(lib, **kw)
+    assert rc == capi.SITU_ERR_INVALID_ARG, (kw, rc)
+    assert capi.last_error(lib) != ""
+
+
+def test_bwd_noalloc_scratch_limit(lib, capi):
+    """One broadcast weight with its gradient keeps one fp32 partial per row in
+    the library's scratch: more rows than SITU_NOALLOC_MAX_ROWS are
+    unsupported (refused before any device work); a per-row weight needs no
+    scratch at any row count."""
+    big = capi.SITU_NOALLOC_MAX_ROWS + 1
+    assert _bwd_noalloc(lib, rows=big, rw_rows=1) == capi.SITU_ERR_UNSUPPORTED
+    assert "SITU_NOALLOC_MAX_ROWS" in capi.last_error(lib)
+    # no d_routing_weights: no scratch, so validation goes on to the other checks
+    assert _bwd_noalloc(lib, rows=big, rw_rows=1, drw=None, go=None) == capi.SITU_ERR_INVALID_ARG
+
+
 def _bwd_mx(lib, **kw):
     # gate_up 4 x 2 x 40 bf16 = 640 bytes at FAKE; rw at FAKE + 4096; grad_out 320 bytes at FAKE + 8192;
     # d_codes 4 x 80 = 320 bytes at FAKE + 16384; d_scales 4 x 4 = 16 bytes at FAKE + 20480;
