@@ -140,6 +140,31 @@ def test_bwd_noalloc_scratch_limit(lib, capi):
     assert _bwd_noalloc(lib, rows=big, rw_rows=1, drw=None, go=None) == capi.SITU_ERR_INVALID_ARG
 
 
+def test_beta_is_a_double(lib, capi):
+    """beta and linear_beta cross the boundary as C doubles, the type of the
+    pages' Python float arguments (a deliberate widening of a C float):
+    values beyond float's range are finite, positive and accepted (an empty
+    call checks them and launches nothing); infinities are rejected."""
+    assert _fwd(lib, rows=0, rw_rows=0, beta=1e39, lb=1e39) == capi.SITU_OK
+    assert _fwd(lib, rows=0, rw_rows=0, beta=math.inf) == capi.SITU_ERR_INVALID_ARG
+    out = (ctypes.c_float * 8)()
+    # a beta that differs from 4 below float's resolution is a different beta (not the b1 = 4 path)
+    assert lib.situ_glu_gate_window(4.0 + 1e-12, out) == capi.SITU_OK
+
+
+def test_pointers_must_be_element_aligned(lib, capi):
+    """Any element-aligned address is accepted (16-byte alignment selects the
+    128-bit path, anything else the element path); an address that is not a
+    multiple of the element size is rejected, a deliberate narrowing: no
+    tensor of that dtype can start there."""
+    assert _fwd(lib, gate_up=FAKE + 1) == capi.SITU_ERR_INVALID_ARG
+    assert "aligned" in capi.last_error(lib)
+    assert _fwd(lib, io=0, gate_up=FAKE + 2) == capi.SITU_ERR_INVALID_ARG      # fp32 at a 2-byte address
+    assert _bwd(lib, go=FAKE + 8193) == capi.SITU_ERR_INVALID_ARG
+    assert "aligned" in capi.last_error(lib)
+    assert _bwd(lib, rw=FAKE + 4097) == capi.SITU_ERR_INVALID_ARG
+
+
 def _bwd_mx(lib, **kw):
     # gate_up 4 x 2 x 40 bf16 = 640 bytes at FAKE; rw at FAKE + 4096; grad_out 320 bytes at FAKE + 8192;
     # d_codes 4 x 80 = 320 bytes at FAKE + 16384; d_scales 4 x 4 = 16 bytes at FAKE + 20480;
