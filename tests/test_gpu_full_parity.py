@@ -63,3 +63,38 @@ def test_every_element_full_size(name):
           f"max dr error / scale {worst['dr']:.2e}", flush=True)
     del x, gu, rw, go, y, dgu, drw
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("inter", [2048, 18432])
+def test_broadcast_dr_at_full_rows(inter):
+    """One routing weight broadcast over all 16384 rows of the dense-FFN
+    recipe, with its gradient (the sum over every row): the per-row partials
+    of the row-mapped kernel and the fixed-order second pass over 16384 of
+    them (sixteen strided passes per thread of its workgroup).  Every
+    element of d_gate_up against the oracle, and the one dr at the parity
+    bar (1e-4 of the sum of |go T_g T_u| over all rows, plus one ulp).
+    inter = 18432 is the full dense-FFN shape."""
+    from ffn_gated_activation_amd import situ_glu_bwd
+    from ffn_gated_activation_amd.workloads import make_inputs
+    print(f"[full] broadcast dr 16384 x {inter}", flush=True)
+    x = make_inputs("dense_ffn", device=DEV, seed=0, inter=inter)
+    gu, go = x["gate_up"], x["grad_out"]
+    rw = torch.tensor([0.625], device=DEV)
+    dgu, drw = situ_glu_bwd(gu, rw, go, 4.0, None, want_drw=True)
+    torch.cuda.synchronize()
+    rows = gu.shape[0]
+    step = max(1, CHUNK_ELEMS // inter)
+    total, total_abs, worst = 0.0, 0.0, 0
+    for lo in range(0, rows, step):
+        hi = min(rows, lo + step)
+        # one broadcast weight over the chunk's rows: dr = the chunk's sum, dr_abs per row
+        ref = oracle_results(gu[lo:hi], rw, go[lo:hi], 4.0, None, True)
+        tag = f"bcast-dr[{lo}:{hi}]"
+        worst = max(worst, assert_close(f"{tag} dG", dgu[lo:hi, :inter], ref["dgu"][:, :inter], ref["dg_scale"]))
+        worst = max(worst, assert_close(f"{tag} dU", dgu[lo:hi, inter:], ref["dgu"][:, inter:]))
+        total += float(ref["dr"][0])
+        total_abs += float(np.sum(ref["dr_abs"]))
+    err = assert_dr_close("bcast dr", drw.reshape(1), np.array([total]), np.array([total_abs]))
+    print(f"[full] broadcast dr 16384 x {inter} ok: max bf16 ulp {worst}, dr {float(drw):.6g} vs {total:.6g}, "
+          f"error / scale {err:.2e}", flush=True)
+
