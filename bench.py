@@ -308,7 +308,7 @@ def bench_attn_res(args) -> int:
         "clock_settle_ms": round(settle_ms, 1),
         "host": _host_info(),
         "kernels": {"attn_res": {"ms": round(k_ms, 5), "bytes": nbytes, "GB/s": round(achieved, 2)}},
-        "roofline": {"bound": "hbm", "kernel": "situ_glu_attn_res_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "situ_glu_attn_res_stream_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(args.workload, "attn_res", ARES_KERNEL_SOURCE)},
         "cpu_baseline": None if args.no_cpu_baseline else _cpu_baseline_attn_res(args.workload),
@@ -701,9 +701,9 @@ def _elementwise(name: str, args, dev, full: bool) -> tuple:
     dom = "bwd" if w.backward else "fwd"
     dom_ms = bwd_ms if w.backward else fwd_ms
     achieved = ab[dom] / (dom_ms / 1e3) / 1e9
-    kname = ("situ_glu_bwd_mx_kernel" if w.backward and w.mx else
+    kname = ("situ_glu_bwd_mx_vec_kernel" if w.backward and w.mx else
              ("situ_glu_bwd_dr_kernel" if want else "situ_glu_bwd_kernel") if w.backward else
-             "situ_glu_fwd_mx_kernel" if w.mx else "situ_glu_fwd_kernel")
+             "situ_glu_fwd_mx_vec_kernel" if w.mx else "situ_glu_fwd_kernel")
     src = MX_KERNEL_SOURCE if w.mx else KERNEL_SOURCE
     rec = {
         "value": round(value, 2),
