@@ -703,7 +703,7 @@ def _elementwise(name: str, args, dev, full: bool) -> tuple:
     achieved = ab[dom] / (dom_ms / 1e3) / 1e9
     kname = ("situ_glu_bwd_mx_vec_kernel" if w.backward and w.mx else
              ("situ_glu_bwd_dr_kernel" if want else "situ_glu_bwd_kernel") if w.backward else
-             "situ_glu_fwd_mx_vec_kernel" if w.mx else "situ_glu_fwd_kernel")
+             "situ_glu_fwd_mx_kernel" if w.mx else "situ_glu_fwd_kernel")
     src = MX_KERNEL_SOURCE if w.mx else KERNEL_SOURCE
     rec = {
         "value": round(value, 2),

@@ -270,8 +270,18 @@ UpK make_up_consts(double beta2)
     UpK k{};
     k.beta2 = (float)beta2;
     k.ku = (float)(2.0L / (long double)beta2 * 1.4426950408889634073599L);
-    k.inv_b2 = (float)(1.0L / (long double)beta2);
-    k.small_max = (float)(0.25L * (long double)beta2);
+    const long double b = beta2, ib = 1.0L / b, ib2 = ib * ib;
+    const long double p[4] = {ib, -ib * ib2 / 3.0L, 2.0L * ib * ib2 * ib2 / 15.0L,
+                              -17.0L * ib * ib2 * ib2 * ib2 / 315.0L};
+    bool normal = true;
+    for (long double c : p)
+        normal = normal && std::isnormal((float)c);
+    k.inv_b2 = (float)ib;
+    k.p1 = (float)p[0];
+    k.p3 = (float)p[1];
+    k.p5 = (float)p[2];
+    k.p7 = (float)p[3];
+    k.small_max = normal ? (float)(0.25L * b) : -1.0f;
     return k;
 }
 
@@ -664,6 +674,8 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t 
     L.fmt = fp8_format == SITU_FP8_E5M2 ? situ::FP8_E5M2 : situ::FP8_E4M3;
     L.ceil_mode = scale_mode == SITU_MX_SCALE_CEIL;
     L.rows_per_block = rows_per_block_override();
+    if (L.vec && (rc = plan_split(rows, intermediate, es, false, L.lb, false, L.split)))
+        return rc;
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);
     const int err = situ::launch_fwd_mx(L, stream);

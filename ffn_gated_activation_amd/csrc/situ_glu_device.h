@@ -197,10 +197,26 @@ __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const 
     }
 }
 
+// tanh(U / b2) for |U| <= b2 / 4 as U P(U^2), the powers of 1/b2 folded
+// into P (UpK): the odd Taylor series of tanh through x^5 (DEG 5: the first
+// dropped term, 17 x^7 / 315, stays below 1.4e-5 of tanh there) or through
+// x^7 (DEG 7: below 3.3e-7).  No exponential, no reciprocal and no
+// cancellation for small U.
+template <int DEG>
+__device__ __forceinline__ float tanh_up(float u, const UpK &k)
+{
+    static_assert(DEG == 5 || DEG == 7, "degree 5 or 7");
+    const float w = u * u;
+    float p = DEG == 7 ? fmaf(k.p7, w, k.p5) : k.p5;
+    p = fmaf(p, w, k.p3);
+    p = fmaf(p, w, k.p1);
+    return u * p;
+}
+
 // tanh(x) for |x| <= 1/4: the odd Taylor polynomial through x^9 (tanh's
 // series x - x^3/3 + 2x^5/15 - 17x^7/315 + 62x^9/2835 - ...; the first term
-// dropped is below 1e-8 of tanh there; fp32 evaluation adds ~3 ulp).  No
-// exponential, no reciprocal, no cancellation for small x.
+// dropped is below 1e-8 of tanh there; fp32 evaluation adds ~3 ulp).  The
+// backward's form (x = U / b2): measured faster there than tanh_up.
 __device__ __forceinline__ float tanh_small(float x)
 {
     const float x2 = x * x;
@@ -208,15 +224,17 @@ __device__ __forceinline__ float tanh_small(float x)
     return fmaf(x * x2, p, x);
 }
 
-// Forward with the up branch as tanh_small(U / b2) (bf16 io, |U| <= b2 / 4):
-// one reciprocal of (1 + e1)(1 + e2) only.
-template <bool FAST>
+// Forward with the up branch as tanh_up (bf16 io, |U| <= b2 / 4): one
+// reciprocal of (1 + e1)(1 + e2) only.  Degree 5 is ample for a bf16 result
+// (its ulp is 2^-8 relative); an fp32 Y that is quantised further (MXFP8)
+// takes degree 7, inside the fp32 chain's 1e-5.
+template <bool FAST, int DEG = 5>
 __device__ __forceinline__ float fwd_elem_small_u(float g, float u, float rscale, const GateK &gk, const UpK &uk)
 {
     const Gate t = gate_parts<FAST, false>(g, rscale, gk);
     const float a = 1.0f + t.e1;
     const float q = rcp(fmaf(t.e2, a, a));  // 1 / ((1 + e1)(1 + e2))
-    return (t.nt * t.sn_s) * (tanh_small(u * uk.inv_b2) * q);
+    return (t.nt * t.sn_s) * (tanh_up<DEG>(u, uk) * q);
 }
 
 // dT_g/dG / 4 near its root, where its two terms cancel.  fp32 io: the

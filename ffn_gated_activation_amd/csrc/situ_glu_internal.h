@@ -30,13 +30,19 @@ struct GateK {
 
 // Up-branch constants (only used when linear_beta is given):
 //   v = exp(-2|U|/b2) = exp2(-|U| * ku)
-// and for the bf16-io kernels' polynomial tanh(U/b2), valid for
-// |U| <= small_max = b2/4: x = U * inv_b2.
+// and for the bf16-io kernels' polynomial tanh(U/b2): x = U * inv_b2 (the
+// backward) or U P(U^2) (the forwards), valid for
+// |U| <= small_max = b2/4, the odd Taylor coefficients of tanh with the
+// powers of 1/b2 folded in: P(w) = p1 + p3 w + p5 w^2 + p7 w^3,
+// p1 = 1/b2, p3 = -1/(3 b2^3), p5 = 2/(15 b2^5), p7 = -17/(315 b2^7).
+// small_max < 0 (the polynomial never taken) when a coefficient is not a
+// normal float.
 struct UpK {
     float beta2;
     float ku;
     float inv_b2;
     float small_max;
+    float p1, p3, p5, p7;
 };
 
 enum { IO_F32 = 0, IO_BF16 = 1 };
@@ -124,7 +130,8 @@ struct FwdMxLaunch {
     int fast;
     int fmt;              // FP8_E4M3 / FP8_E5M2
     int ceil_mode;        // 0: floor(log2 amax) - emax, 1: no element saturates
-    int rows_per_block;
+    int rows_per_block;   // element path
+    ChunkSplit split;     // 128-bit path
     GateK gk;
     UpK uk;
 };

@@ -31,41 +31,15 @@
 #include <mutex>
 
 #include "situ_glu.h"
+#include "situ_glu_chunk.h"
 #include "situ_glu_device.h"
 #include "situ_glu_internal.h"
 
 namespace situ {
 namespace {
 
-constexpr uint32_t kChunkBytes = 1024;  // 64 lanes x 16 bytes of each stream
-
-// One chunk's streams: buffer descriptors (range = the chunk, or empty for a
-// chunk past the wavefront's share: loads return zeros, stores are dropped)
-// and the bits of the row's routing weight (fp32, or bf16 in the low half),
-// converted only by the chunk's math.  The weight's dtype is a template
-// parameter (RWB: bf16), so that no chunk's loads wait behind a branch on it
-// or behind the weight's own load.
-template <int NIN, int NOUT>
-struct Chunk {
-    rsrc_t in[NIN];
-    rsrc_t out[NOUT];
-    uint32_t rbits;
-};
-
-template <bool RWB>
-__device__ __forceinline__ float weight_of(uint32_t rbits)
-{
-    return __uint_as_float(RWB ? rbits << 16 : rbits);
-}
-
 // Streams of chunk c of a row.  NIN = 2: gate_up halves; 3: plus grad_out.
 // NOUT = 1: out [rows, I]; 2: d_gate_up halves.
-template <bool RWB>
-__device__ __forceinline__ uint32_t weight_bits(const void *rw, int64_t i)
-{
-    return RWB ? (uint32_t)static_cast<const uint16_t *>(rw)[i] : static_cast<const uint32_t *>(rw)[i];
-}
-
 template <int NIN, int NOUT>
 __device__ __forceinline__ Chunk<NIN, NOUT> chunk_at(int64_t row, uint32_t c, bool live, const ChunkGeom &g,
                                                       const char *gu, const char *go, char *o, uint32_t rbits)
@@ -89,26 +63,6 @@ __device__ __forceinline__ Chunk<NIN, NOUT> chunk_at(int64_t row, uint32_t c, bo
     }
     k.rbits = rbits;
     return k;
-}
-
-// Fences that keep each chunk's loads ahead of the previous chunk's math, as
-// written: the scheduling barrier within a block, and an empty statement
-// that may touch memory, so that no load is sunk past a branch of the math
-// (it emits no instruction).
-__device__ __forceinline__ void order_fence()
-{
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-}
-
-// Issue one chunk's loads.
-template <int NIN, int NOUT>
-__device__ __forceinline__ void load_chunk(uint4 *v, const Chunk<NIN, NOUT> &k, uint32_t voff)
-{
-#pragma unroll
-    for (int i = 0; i < NIN; ++i)
-        v[i] = bload(k.in[i], voff);
-    order_fence();
 }
 
 template <int IO, bool LB, bool FAST, bool RWB>
@@ -182,43 +136,6 @@ __device__ __forceinline__ void bwd_chunk(const uint4 *v, const Chunk<3, 2> &k, 
     order_fence();
 }
 
-// chunk index -> (row, chunk in row)
-__device__ __forceinline__ void locate(uint32_t u, const ChunkGeom &g, int64_t &row, uint32_t &c)
-{
-    const uint32_t q = g.cpr == 1 ? u : __umulhi(u, g.magic) >> g.shift;
-    row = q;
-    c = u - q * (uint32_t)g.cpr;
-}
-
-// The wavefront's n chunks (n >= 1), two register sets: the loads of chunk
-// i + 1 are in flight during chunk i's math.  `step(row, c)` moves to the
-// next chunk.  WEIGHT(row) gives the row's weight bits; BODY(regs, chunk) is
-// the math and the stores.
-#define SITU_CHUNK_PIPELINE(NIN, NOUT, WEIGHT, BODY)                                                       \
-    {                                                                                             \
-        uint4 A[NIN], B[NIN];                                                                     \
-        Chunk<NIN, NOUT> ka = chunk_at<NIN, NOUT>(row, c, true, g, gp, gop, op, WEIGHT(row)); \
-        load_chunk(A, ka, voff);                                                                  \
-        step(row, c);                                                                             \
-        Chunk<NIN, NOUT> kb = chunk_at<NIN, NOUT>(row, c, 1 < n, g, gp, gop, op, WEIGHT(row)); \
-        load_chunk(B, kb, voff);                                                                  \
-        BODY(A, ka);                                                                              \
-        int i = 1;                                                                                \
-        for (; i + 2 <= n; i += 2) {                                                              \
-            step(row, c);                                                                         \
-            ka = chunk_at<NIN, NOUT>(row, c, i + 1 < n, g, gp, gop, op, WEIGHT(row));  \
-            load_chunk(A, ka, voff);                                                              \
-            BODY(B, kb);                                                                          \
-            step(row, c);                                                                         \
-            kb = chunk_at<NIN, NOUT>(row, c, i + 2 < n, g, gp, gop, op, WEIGHT(row));  \
-            load_chunk(B, kb, voff);                                                              \
-            BODY(A, ka);                                                                          \
-        }                                                                                         \
-        if (i < n) {                                                                              \
-            BODY(B, kb);                                                                          \
-        }                                                                                         \
-    }
-
 // Forward, flat mapping: wavefront w takes chunks w k .. w k + k - 1 of the
 // `total` chunks of the tensor.
 template <int IO, bool LB, bool FAST, bool RWB>
@@ -244,9 +161,9 @@ situ_glu_fwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ r
     const char *gop = nullptr;
     char *op = static_cast<char *>(out);
 #define SITU_FWD_BODY(R, K) fwd_chunk<IO, LB, FAST, RWB>(R, K, voff, gk, uk)
-#define SITU_WEIGHT(R) weight_bits<RWB>(rw, (R) * rw_stride)
-    SITU_CHUNK_PIPELINE(2, 1, SITU_WEIGHT, SITU_FWD_BODY)
-#undef SITU_WEIGHT
+#define SITU_MAKE(R, C, L) chunk_at<2, 1>(R, C, L, g, gp, gop, op, weight_bits<RWB>(rw, (R) * rw_stride))
+    SITU_CHUNK_PIPELINE(2, 1, SITU_MAKE, SITU_FWD_BODY)
+#undef SITU_MAKE
 #undef SITU_FWD_BODY
 }
 
@@ -282,9 +199,9 @@ situ_glu_bwd_kernel(const void *__restrict__ gate_up, const void *__restrict__ r
     char *op = static_cast<char *>(d_gate_up);
     float acc = 0.0f;
 #define SITU_BWD_BODY(R, K) bwd_chunk<IO, LB, FAST, RWB, false>(R, K, voff, gk, uk, acc)
-#define SITU_WEIGHT(R) weight_bits<RWB>(rw, (R) * rw_stride)
-    SITU_CHUNK_PIPELINE(3, 2, SITU_WEIGHT, SITU_BWD_BODY)
-#undef SITU_WEIGHT
+#define SITU_MAKE(R, C, L) chunk_at<3, 2>(R, C, L, g, gp, gop, op, weight_bits<RWB>(rw, (R) * rw_stride))
+    SITU_CHUNK_PIPELINE(3, 2, SITU_MAKE, SITU_BWD_BODY)
+#undef SITU_MAKE
 #undef SITU_BWD_BODY
 }
 
@@ -320,9 +237,9 @@ situ_glu_bwd_dr_kernel(const void *__restrict__ gate_up, const void *__restrict_
         char *op = static_cast<char *>(d_gate_up);
         const uint32_t rb = weight_bits<RWB>(rw, row * rw_stride);  // one row: one weight
 #define SITU_BWD_BODY(R, K) bwd_chunk<IO, LB, FAST, RWB, true>(R, K, voff, gk, uk, acc)
-#define SITU_WEIGHT(R) rb
-        SITU_CHUNK_PIPELINE(3, 2, SITU_WEIGHT, SITU_BWD_BODY)
-#undef SITU_WEIGHT
+#define SITU_MAKE(R, C, L) chunk_at<3, 2>(R, C, L, g, gp, gop, op, rb)
+        SITU_CHUNK_PIPELINE(3, 2, SITU_MAKE, SITU_BWD_BODY)
+#undef SITU_MAKE
 #undef SITU_BWD_BODY
     }
     const float scale = LB ? gk.beta1 * uk.beta2 : gk.beta1;

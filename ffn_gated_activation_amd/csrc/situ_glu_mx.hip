@@ -22,8 +22,11 @@
 // Layout: codes [rows, cols] bytes (row major, one byte per value), scales
 // [rows, ceil(cols / 32)] bytes.
 //
-// Work decomposition as the bf16 forward: strips of 64 lanes x 4 128-bit
-// vectors per wavefront.  A lane holds 8 (bf16) or 4 (fp32) consecutive
+// Work decomposition: the forward takes the bf16 forward's chunk layout (a
+// chunk is 64 lanes x one 128-bit vector of each half row, k consecutive
+// chunks per wavefront, the next chunk's loads issued before the current
+// chunk's math); the backward and the stand-alone quantiser strips of 64
+// lanes x 2 or 4 vectors per wavefront.  A lane holds 8 (bf16) or 4 (fp32) consecutive
 // values of a vector, so a block of 32 is 4 or 8 neighbouring lanes: their
 // largest magnitude meets through DPP lane swaps, inside the quad (and the
 // half row for 8 lanes).  Values are converted two at a time by gfx950's
@@ -37,6 +40,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "situ_glu_chunk.h"
 #include "situ_glu_device.h"
 #include "situ_glu_internal.h"
 
@@ -181,52 +185,93 @@ __device__ __forceinline__ unsigned char encode1(float y, uint32_t code)
 
 // ---------------------------------------------------------------- kernels
 
-// Fused forward, 128-bit path (same placement as the bf16 forward).
-template <int IO, bool LB, bool FAST, int FMT, int MODE>
-__global__ void __launch_bounds__(64 * kMaxWaves)
-situ_glu_fwd_mx_vec_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int rw_bf16,
-                           int64_t rw_stride, unsigned char *__restrict__ codes, unsigned char *__restrict__ scales,
-                           int64_t rows, int inter, int waves_per_row, GateK gk, UpK uk)
+// Streams of chunk c of a row for the fused forward: the gate and up halves
+// in, the chunk's element codes (kChunkBytes / element size of them) and
+// block scales out.
+template <int IO>
+__device__ __forceinline__ Chunk<2, 2> mx_chunk_at(int64_t row, uint32_t c, bool live, const ChunkGeom &g,
+                                                   const char *gu, unsigned char *codes, unsigned char *scales,
+                                                   uint32_t inter, uint32_t nblk, uint32_t rbits)
 {
-    constexpr bool PRECISE = IO == IO_F32;
+    constexpr uint32_t kVals = kChunkBytes / Io<IO>::kBytes, kBlocks = kVals / kMxBlock;
+    Chunk<2, 2> k;
+    const uint32_t off = c * kChunkBytes;
+    const uint32_t left = g.half - off;
+    const uint32_t n = live ? (left < kChunkBytes ? left : kChunkBytes) : 0u;
+    const uint32_t v0 = c * kVals, b0 = c * kBlocks;
+    const uint32_t nv = live ? (inter - v0 < kVals ? inter - v0 : kVals) : 0u;
+    const uint32_t nb = live ? (nblk - b0 < kBlocks ? nblk - b0 : kBlocks) : 0u;
+    row = live ? row : 0;
+    const char *gr = gu + row * (int64_t)g.half * 2 + off;
+    k.in[0] = make_rsrc(gr, n);
+    k.in[1] = make_rsrc(gr + g.half, n);
+    k.out[0] = make_rsrc(codes + row * (int64_t)inter + v0, nv);
+    k.out[1] = make_rsrc(scales + row * (int64_t)nblk + b0, nb);
+    k.rbits = rbits;
+    return k;
+}
+
+// One chunk of the fused forward: Y in fp32, then its blocks quantised.  bf16
+// io with a linear beta takes the polynomial up branch when the wavefront's
+// |U| allow it (degree 7: the fp32 Y stays inside the chain's 1e-5).  Past
+// the row end the loads returned zeros: Y = 0 there, which leaves every
+// block maximum unchanged, and the stores are dropped.
+template <int IO, bool LB, bool FAST, bool RWB, int FMT, int MODE>
+__device__ __forceinline__ void fwd_mx_chunk(const uint4 *v, const Chunk<2, 2> &k, int lane, const GateK &gk,
+                                             const UpK &uk)
+{
     using T = Io<IO>;
     constexpr int E = T::kPerVec;
-    constexpr int kStrip = 64 * kUnrollMx;
-    const int lane = threadIdx.x & 63;
-    const Place pl = place(waves_per_row);
-    if (pl.row >= rows)
-        return;
-    const int nv = inter / E;
-    const uint32_t half = (uint32_t)nv * 16u;
-    const int nblk = (inter + kMxBlock - 1) / kMxBlock;
-    const int spr = (nv + kStrip - 1) / kStrip;
-    const char *row = static_cast<const char *>(gate_up) + pl.row * (int64_t)half * 2;
-    const rsrc_t rg = make_rsrc(row, half), ru = make_rsrc(row + half, half);
-    const rsrc_t rc = make_rsrc(codes + pl.row * (int64_t)inter, (uint32_t)inter);
-    const rsrc_t rs = make_rsrc(scales + pl.row * (int64_t)nblk, (uint32_t)nblk);
-    const float r = load_rw(rw, rw_bf16, pl.row * rw_stride);
+    const float r = weight_of<RWB>(k.rbits);
     const float rscale = LB ? r * gk.beta1 * uk.beta2 : r * gk.beta1;
-    for (int s = pl.strip0; s < spr; s += pl.wpr) {
-        uint4 gv[kUnrollMx], uv[kUnrollMx];
+    float g[E], u[E], y[E];
+    T::unpack(v[0], g);
+    T::unpack(v[1], u);
+    if (LB && IO == IO_BF16 && wave_up_small<E>(u, uk)) {
 #pragma unroll
-        for (int k = 0; k < kUnrollMx; ++k) {
-            const uint32_t off = (uint32_t)(s * kStrip + 64 * k + lane) * 16u;
-            gv[k] = bload(rg, off);
-            uv[k] = bload(ru, off);
-        }
+        for (int e = 0; e < E; ++e)
+            y[e] = fwd_elem_small_u<FAST, 7>(g[e], u[e], rscale, gk, uk);
+    } else {
 #pragma unroll
-        for (int k = 0; k < kUnrollMx; ++k) {
-            // past the row end the loads returned zeros: Y = 0 there, which
-            // leaves every block maximum unchanged, and the stores are dropped
-            float g[E], u[E], y[E];
-            T::unpack(gv[k], g);
-            T::unpack(uv[k], u);
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                y[e] = fwd_elem<LB, FAST, PRECISE>(g[e], u[e], rscale, gk, uk);
-            quantize_vector<FMT, MODE, E>(y, s * kStrip + 64 * k + lane, lane, rc, rs);
-        }
+        for (int e = 0; e < E; ++e)
+            y[e] = fwd_elem<LB, FAST, IO == IO_F32>(g[e], u[e], rscale, gk, uk);
     }
+    quantize_vector<FMT, MODE, E>(y, lane, lane, k.out[0], k.out[1]);
+    order_fence();
+}
+
+// Fused forward, 128-bit path: flat chunk mapping, wavefront w takes chunks
+// w k .. w k + k - 1 of the `total` chunks.
+template <int IO, bool LB, bool FAST, bool RWB, int FMT, int MODE>
+__global__ void __launch_bounds__(256)
+situ_glu_fwd_mx_kernel(const void *__restrict__ gate_up, const void *__restrict__ rw, int64_t rw_stride,
+                       unsigned char *__restrict__ codes, unsigned char *__restrict__ scales, uint32_t inter,
+                       uint32_t total, ChunkGeom g, GateK gk, UpK uk)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t voff = (uint32_t)lane * 16u;
+    const uint32_t gw = blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t first = gw * (uint32_t)g.k;
+    if (first >= total)
+        return;
+    const int n = total - first < (uint32_t)g.k ? (int)(total - first) : g.k;
+    const uint32_t nblk = (inter + kMxBlock - 1) / kMxBlock;
+    int64_t row;
+    uint32_t c;
+    locate(first, g, row, c);
+    auto step = [&](int64_t &r_, uint32_t &c_) {
+        if (++c_ == (uint32_t)g.cpr) {
+            c_ = 0;
+            ++r_;
+        }
+    };
+    const char *gp = static_cast<const char *>(gate_up);
+#define SITU_MX_BODY(R, K) fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE>(R, K, lane, gk, uk)
+#define SITU_MAKE(R, C, L) \
+    mx_chunk_at<IO>(R, C, L, g, gp, codes, scales, inter, nblk, weight_bits<RWB>(rw, (R) * rw_stride))
+    SITU_CHUNK_PIPELINE(2, 2, SITU_MAKE, SITU_MX_BODY)
+#undef SITU_MAKE
+#undef SITU_MX_BODY
 }
 
 // Largest value over each half wavefront (lanes 0-31, 32-63).
@@ -493,14 +538,6 @@ using QuantFn = void (*)(const void *, unsigned char *, unsigned char *, int64_t
 using BwdMxFn = void (*)(const void *, const void *, int, int64_t, const void *, unsigned char *, unsigned char *,
                          void *, float *, int64_t, int, int, GateK, UpK);
 
-template <int IO, bool VEC, bool LB, bool FAST, int FMT, int MODE>
-constexpr FwdMxFn fwd_mx_fn()
-{
-    if constexpr (VEC)
-        return situ_glu_fwd_mx_vec_kernel<IO, LB, FAST, FMT, MODE>;
-    else
-        return situ_glu_fwd_mx_elem_kernel<IO, LB, FAST, FMT, MODE>;
-}
 template <int IO, bool VEC, int FMT, int MODE>
 constexpr QuantFn quant_fn()
 {
@@ -510,16 +547,25 @@ constexpr QuantFn quant_fn()
         return situ_glu_mx_quant_elem_kernel<IO, FMT, MODE>;
 }
 
-#define SITU_MX_FM(IO, VEC, LB, FAST, FMT) {fwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_FLOOR>(), fwd_mx_fn<IO, VEC, LB, FAST, FMT, MX_CEIL>()}
-#define SITU_MX_CASE(IO, VEC, LB, FAST) {SITU_MX_FM(IO, VEC, LB, FAST, FP8_E4M3), SITU_MX_FM(IO, VEC, LB, FAST, FP8_E5M2)}
-#define SITU_MX_ROW(IO, VEC)                                                                         \
-    { SITU_MX_CASE(IO, VEC, false, false), SITU_MX_CASE(IO, VEC, false, true),                      \
-      SITU_MX_CASE(IO, VEC, true, false), SITU_MX_CASE(IO, VEC, true, true) }
-// index: [io][vec][lb * 2 + fast][fmt][mode]
-const FwdMxFn kFwdMx[2][2][4][2][2] = {
-    {SITU_MX_ROW(IO_F32, false), SITU_MX_ROW(IO_F32, true)},
-    {SITU_MX_ROW(IO_BF16, false), SITU_MX_ROW(IO_BF16, true)},
-};
+// element path: index [io][lb * 2 + fast][fmt][mode]
+#define SITU_MXE_FM(IO, LB, FAST, FMT)                                                                \
+    {situ_glu_fwd_mx_elem_kernel<IO, LB, FAST, FMT, MX_FLOOR>, situ_glu_fwd_mx_elem_kernel<IO, LB, FAST, FMT, MX_CEIL>}
+#define SITU_MXE_CASE(IO, LB, FAST) {SITU_MXE_FM(IO, LB, FAST, FP8_E4M3), SITU_MXE_FM(IO, LB, FAST, FP8_E5M2)}
+#define SITU_MXE_ROW(IO)                                                                             \
+    { SITU_MXE_CASE(IO, false, false), SITU_MXE_CASE(IO, false, true), SITU_MXE_CASE(IO, true, false), \
+      SITU_MXE_CASE(IO, true, true) }
+const FwdMxFn kFwdMxElem[2][4][2][2] = {SITU_MXE_ROW(IO_F32), SITU_MXE_ROW(IO_BF16)};
+// 128-bit path: index [io][rw bf16][lb * 2 + fast][fmt][mode]
+#define SITU_MXV_FM(IO, RWB, LB, FAST, FMT)                                                          \
+    {situ_glu_fwd_mx_kernel<IO, LB, FAST, RWB, FMT, MX_FLOOR>, situ_glu_fwd_mx_kernel<IO, LB, FAST, RWB, FMT, MX_CEIL>}
+#define SITU_MXV_CASE(IO, RWB, LB, FAST) {SITU_MXV_FM(IO, RWB, LB, FAST, FP8_E4M3), SITU_MXV_FM(IO, RWB, LB, FAST, FP8_E5M2)}
+#define SITU_MXV_RW(IO, RWB)                                                                         \
+    { SITU_MXV_CASE(IO, RWB, false, false), SITU_MXV_CASE(IO, RWB, false, true),                       \
+      SITU_MXV_CASE(IO, RWB, true, false), SITU_MXV_CASE(IO, RWB, true, true) }
+using FwdMxVecFn = void (*)(const void *, const void *, int64_t, unsigned char *, unsigned char *, uint32_t, uint32_t,
+                            ChunkGeom, GateK, UpK);
+const FwdMxVecFn kFwdMxVec[2][2][4][2][2] = {{SITU_MXV_RW(IO_F32, false), SITU_MXV_RW(IO_F32, true)},
+                                             {SITU_MXV_RW(IO_BF16, false), SITU_MXV_RW(IO_BF16, true)}};
 template <int IO, bool VEC, bool LB, bool FAST, int FMT, int MODE>
 constexpr BwdMxFn bwd_mx_fn()
 {
@@ -551,11 +597,18 @@ const QuantFn kQuant[2][2][2][2] = {
 
 int launch_fwd_mx(const FwdMxLaunch &L, void *stream)
 {
-    const Shape sh = shape(L.rows, L.inter, L.io, L.vec, L.rows_per_block, kUnrollMx);
-    const FwdMxFn fn = kFwdMx[L.io][L.vec][L.lb * 2 + L.fast][L.fmt][L.ceil_mode ? MX_CEIL : MX_FLOOR];
-    hipLaunchKernelGGL(fn, sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up, L.rw, L.rw_bf16, L.rw_stride,
-                       static_cast<unsigned char *>(L.codes), static_cast<unsigned char *>(L.scales), L.rows,
-                       L.inter, sh.waves_per_row, L.gk, L.uk);
+    const int v = L.lb * 2 + L.fast, mode = L.ceil_mode ? MX_CEIL : MX_FLOOR;
+    if (L.vec) {
+        hipLaunchKernelGGL(kFwdMxVec[L.io][L.rw_bf16][v][L.fmt][mode], dim3(L.split.grid), dim3(L.split.block), 0,
+                           (hipStream_t)stream, L.gate_up, L.rw, L.rw_stride, static_cast<unsigned char *>(L.codes),
+                           static_cast<unsigned char *>(L.scales), (uint32_t)L.inter, L.split.total, L.split.geom,
+                           L.gk, L.uk);
+    } else {
+        const Shape sh = shape(L.rows, L.inter, L.io, 0, L.rows_per_block, kUnrollMx);
+        hipLaunchKernelGGL(kFwdMxElem[L.io][v][L.fmt][mode], sh.grid, sh.block, 0, (hipStream_t)stream, L.gate_up,
+                           L.rw, L.rw_bf16, L.rw_stride, static_cast<unsigned char *>(L.codes),
+                           static_cast<unsigned char *>(L.scales), L.rows, L.inter, sh.waves_per_row, L.gk, L.uk);
+    }
     return (int)hipGetLastError();
 }
 
