@@ -289,9 +289,10 @@ UpK make_up_consts(double beta2)
 
 namespace {
 
-// Rows per workgroup of the 128-bit path when a row is one strip: 0 lets the
-// launcher choose; the environment variable SITU_GLU_ROWS_PER_BLOCK (1..16)
-// fixes it (tuning).
+// Rows per workgroup of the strip-layout kernels (the MXFP8 element paths,
+// the MXFP8 backward and the stand-alone quantiser) when a row is one strip:
+// 0 lets the launcher choose; the environment variable
+// SITU_GLU_ROWS_PER_BLOCK (1..16) fixes it (tuning).
 int rows_per_block_override()
 {
     static const int v = [] {

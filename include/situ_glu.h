@@ -25,8 +25,10 @@
  *                    rw_rows == 1 (one weight broadcast over every row)
  *   d_routing_weights[rw_rows]                rw dtype
  * Leading dimensions of [..., 2I] tensors are flattened into `rows` by the
- * caller.  Any pointer alignment is accepted; 16-byte-aligned buffers with
- * intermediate a multiple of 8 (bf16) or 4 (fp32) take the 128-bit path.
+ * caller.  Every pointer must be aligned to its element size (2 bytes for
+ * bf16, 4 for fp32; SITU_ERR_INVALID_ARG otherwise); beyond that any
+ * alignment is accepted, and 16-byte-aligned buffers with intermediate a
+ * multiple of 8 (bf16) or 4 (fp32) take the 128-bit path.
  *
  * Precision: inputs are widened to fp32, every intermediate is fp32 (the
  * NeMo page's fp32 chain over low-precision saved inputs), and results are
@@ -206,8 +208,9 @@ int situ_glu_bwd_noalloc(const void *gate_up, int io_dtype, int64_t rows,
  *   codes            device pointer, [rows, intermediate] bytes (row major)
  *   scales           device pointer, [rows, ceil(intermediate / 32)] bytes
  *   stream           hipStream_t or NULL
- * codes and scales must not overlap the inputs or each other.  Any pointer
- * alignment is accepted; a 16-byte-aligned gate_up with intermediate a
+ * codes and scales must not overlap the inputs or each other.  Input
+ * pointers aligned to their element size; beyond that any alignment is
+ * accepted, and a 16-byte-aligned gate_up with intermediate a
  * multiple of 8 (bf16) or 4 (fp32) and codes aligned to 8 (bf16) or 4 (fp32)
  * bytes take the 128-bit path.  Returns as situ_glu_fwd; an unknown format or
  * mode is SITU_ERR_INVALID_ARG.
@@ -238,8 +241,9 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows,
  *                dG's block scales, then dU's, per row
  *   d_routing_weights, workspace, workspace_bytes, stream   as for
  *                situ_glu_bwd (situ_glu_bwd_workspace_bytes gives the size)
- * Outputs must not overlap the inputs or each other.  Any alignment is
- * accepted; 16-byte-aligned gate_up and grad_out with intermediate a
+ * Outputs must not overlap the inputs or each other.  Input pointers aligned
+ * to their element size; beyond that any alignment is accepted, and
+ * 16-byte-aligned gate_up and grad_out with intermediate a
  * multiple of 8 (bf16) or 4 (fp32) and d_codes aligned to 8 (bf16) or 4
  * (fp32) bytes take the 128-bit path.  Returns as situ_glu_bwd; an unknown
  * format or mode is SITU_ERR_INVALID_ARG.
