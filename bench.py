@@ -368,7 +368,7 @@ def _cold_and_ceilings(kernels: dict, nbytes: dict, rows: int, inter: int, n: in
 def _probe_ceilings(a, n: int, flush) -> dict:
     """The SiTU kernels' access pattern with no arithmetic
     (libsitu_stream_probe.so, built next to the library): 16-byte
-    non-temporal loads and stores, one wavefront per 4 KiB strip of every
+    non-temporal loads and stores, one wavefront per 1 KiB chunk of every
     stream, at the forward's mix (2 read streams : 1 written) and the
     backward's (3 : 2, the routing weights aside), streams of the workload's
     [rows, I] bf16 size.  The memory ceiling of each mix."""

@@ -5,14 +5,12 @@
 // used only to report the memory ceiling of each read:write mix next to
 // the measured kernels.
 //
-// Access pattern, as the 128-bit path of the forward and backward: one
-// 64-lane wavefront per workgroup, each wavefront a strip of 64 lanes x U
-// 16-byte vectors of every stream, all loads issued before the stores, every
-// access through a buffer descriptor with the non-temporal hint.  U = 4 up
-// to three streams (the forward's choice) and 2 beyond (the backward's: five
-// streams of 4 vectors would hold 80 registers a lane and cut the wavefronts
-// per SIMD).  The written value is the xor of the read vectors, so no
-// load can be dropped.
+// Access pattern, as one chunk of the 128-bit path of the forward and
+// backward: one 64-lane wavefront per workgroup, each wavefront one chunk of
+// 64 lanes x one 16-byte vector of every stream (1 KiB per stream), the
+// loads issued before the stores, every access through a buffer descriptor
+// with the non-temporal hint.  The written value is the xor of the read
+// vectors, so no load can be dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,7 +35,7 @@ __device__ __forceinline__ rsrc_t rsrc(const void *p, uint32_t bytes)
 template <int NI, int NO>
 __global__ void __launch_bounds__(64) situ_stream_probe_kernel(Streams s, int64_t nvec)
 {
-    constexpr int kUnroll = NI + NO <= 3 ? 4 : 2;
+    constexpr int kUnroll = 1;
     constexpr int kStripVecs = 64 * kUnroll;
     const int lane = threadIdx.x;
     const int64_t v0 = (int64_t)blockIdx.x * kStripVecs;
@@ -67,7 +65,7 @@ __global__ void __launch_bounds__(64) situ_stream_probe_kernel(Streams s, int64_
 template <int NI, int NO>
 hipError_t launch(const Streams &s, int64_t nvec, hipStream_t st)
 {
-    constexpr int kStripVecs = 64 * (NI + NO <= 3 ? 4 : 2);
+    constexpr int kStripVecs = 64;
     const int64_t blocks = (nvec + kStripVecs - 1) / kStripVecs;
     hipLaunchKernelGGL((situ_stream_probe_kernel<NI, NO>), dim3((unsigned)blocks), dim3(64), 0, st, s, nvec);
     return hipGetLastError();
