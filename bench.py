@@ -32,9 +32,10 @@ synchronisations.  Prints ONE JSON line:
   cold_cache_and_ceilings
                (elementwise workloads) the median of each kernel's launches
                with a 512 MiB read before each one (nothing left in L2 or the
-               Infinity Cache), and a plain copy and bf16 add of the same
-               sizes, warm and cold, as measured ceilings of their read:write
-               mixes
+               Infinity Cache), the same after a 512 MiB write instead
+               (*_cold_after_write: its dirty lines are written back during
+               the launch), and a plain copy and bf16 add of the same sizes,
+               warm and cold, as measured ceilings of their read:write mixes
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -317,18 +318,22 @@ def bench_attn_res(args) -> int:
     return 0
 
 
-def _median_ms(fn, n, flush=None) -> float:
+def _median_ms(fn, n, flush=None, write: bool = False) -> float:
     """Median duration of n launches of fn, each between two HIP events on
     the launch stream; with `flush`, a read of 512 MiB (not timed) runs
     before every launch so that nothing the launch reads is left in L2 or the
     Infinity Cache.  A read, not a fill: a fill leaves up to the Infinity
     Cache's 256 MB of dirty lines, whose write-back the timed launch would
-    then pay for."""
+    then pay for.  `write` takes the fill instead (the literal flush-write of
+    the timing protocol, reported beside the read)."""
     import torch
     ts = []
     for _ in range(n):
         if flush is not None:
-            flush.amax()
+            if write:
+                flush.fill_(1.0)
+            else:
+                flush.amax()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -350,6 +355,9 @@ def _cold_and_ceilings(kernels: dict, nbytes: dict, rows: int, inter: int, n: in
     for name, fn in kernels.items():
         ms = _median_ms(fn, n, flush)
         out[f"{name}_cold"] = {"ms": round(ms, 5), "GB/s": round(nbytes[name] / (ms / 1e3) / 1e9, 2)}
+    for name, fn in kernels.items():
+        ms = _median_ms(fn, n, flush, write=True)
+        out[f"{name}_cold_after_write"] = {"ms": round(ms, 5), "GB/s": round(nbytes[name] / (ms / 1e3) / 1e9, 2)}
     a = torch.empty(rows, inter, dtype=torch.bfloat16, device=dev).normal_()
     b = torch.empty_like(a).normal_()
     c = torch.empty_like(a)
