@@ -152,6 +152,7 @@ __device__ __forceinline__ float scaled_one_minus_exp2_neg(float z, float e, flo
 
 struct Gate {
     float e1, e2, nt;
+    float h;      // exp(-|G| / 2): e2 = h * h
     float sn_s;   // sgn(G) * sigmoid numerator: G < 0 ? -e2 : 1
     float snc_s;  // sgn(G) * sigmoid(-G) numerator: G < 0 ? -1 : e2
 };
@@ -165,17 +166,32 @@ __device__ __forceinline__ Gate gate_parts(float g, float ntscale, const GateK &
     const float z = a * (FAST ? 0.5f * kLog2e : k.k1);  // e1 = 2^-z = exp(-2a/b1)
     o.e1 = ex2(-z);
     if (FAST) {
+        o.h = o.e1;
         o.e2 = o.e1 * o.e1;
     } else {
         // exp(-a) as the square of exp(-a/2): keeps gradual underflow to a ~ 174
-        const float h = ex2(a * (-0.5f * kLog2e));
-        o.e2 = h * h;
+        o.h = ex2(a * (-0.5f * kLog2e));
+        o.e2 = o.h * o.h;
     }
     o.nt = scaled_one_minus_exp2_neg<PRECISE, 1>(z, o.e1, ntscale);
     const bool neg = g < 0.0f;
     o.sn_s = neg ? -o.e2 : 1.0f;
     o.snc_s = neg ? -1.0f : o.e2;
     return o;
+}
+
+// fp32 io, G < 0 with e2 = exp(G) below fp32's normal range: Y = -(nt h)
+// (rest) h, the sigmoid numerator's two factors h multiplied into the
+// already scaled product one at a time, so that Y is rounded once in the
+// subnormal range rather than e2 first and that error then scaled.
+template <bool PRECISE>
+__device__ __forceinline__ float gate_times(const Gate &t, float g, float rest)
+{
+    const float y = (t.nt * t.sn_s) * rest;
+    if (!PRECISE)
+        return y;
+    const float ys = -(((t.nt * t.h) * rest) * t.h);
+    return g < 0.0f && t.e2 < 1.17549435e-38f ? ys : y;
 }
 
 // Y = r T_g T_u: rscale = r b1 b2 (r b1 without linear beta) rides on nt.
@@ -190,10 +206,10 @@ __device__ __forceinline__ float fwd_elem(float g, float u, float rscale, const 
         const float v = ex2(-z);
         const float nu = copysignf(scaled_one_minus_exp2_neg<PRECISE, 1>(z, v, 1.0f), u);
         const float q = rcp(fmaf(m, v, m));  // 1 / ((1 + e1)(1 + e2)(1 + v))
-        return (t.nt * t.sn_s) * (nu * q);
+        return gate_times<PRECISE>(t, g, nu * q);
     } else {
         const float q = rcp(m);
-        return (t.nt * t.sn_s) * (u * q);
+        return gate_times<PRECISE>(t, g, u * q);
     }
 }
 

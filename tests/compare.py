@@ -19,7 +19,10 @@ whose intermediate falls into the subnormal range (T_g ~ -b1 e^G for G below
 about -87, sech^2(U/b2) for |U| above about 44 b2) carries an absolute error of
 a few 2^-149 in that intermediate, which the other (bounded) factors of the
 product then scale: `allow` is that allowance, 64 * 2^-149 times a bound on the
-other factors (subnormal_allowance below).  Only such extreme inputs reach it.
+other factors (subnormal_allowance below), for the backward's products.  The
+fp32 forward multiplies the two factors of e^G into its already scaled
+product one at a time and so rounds Y once in the subnormal range: its
+allowance is 2 * 2^-149.  Only such extreme inputs reach either.
 """
 from __future__ import annotations
 
@@ -73,6 +76,7 @@ def assert_bf16_close(name: str, gpu: torch.Tensor, ref64: np.ndarray, bar: int 
 
 
 SUBNORMAL_QUANTA = 64 * 2.0 ** -149
+Y_SUBNORMAL_QUANTA = 2 * 2.0 ** -149
 
 
 def subnormal_allowance(gate_up64: np.ndarray, r64: np.ndarray, go64: np.ndarray | None, beta: float,
@@ -83,7 +87,7 @@ def subnormal_allowance(gate_up64: np.ndarray, r64: np.ndarray, go64: np.ndarray
     U = np.abs(gate_up64[:, inter:])
     tub = U if linear_beta is None else np.minimum(U, linear_beta)
     r = np.abs(np.broadcast_to(r64.reshape(-1, 1), (gate_up64.shape[0], 1)))
-    out = {"y": SUBNORMAL_QUANTA * r * (tub + beta)}
+    out = {"y": np.full(np.broadcast_shapes(U.shape, r.shape), Y_SUBNORMAL_QUANTA)}
     if go64 is not None:
         go = np.abs(go64)
         out["dG"] = SUBNORMAL_QUANTA * go * r * (tub + 1.0 + beta / 4.0)

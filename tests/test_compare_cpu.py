@@ -154,16 +154,17 @@ def test_dr_bar():
 
 
 def test_subnormal_allowance_values():
-    """64 subnormal quanta times the bound of the other factors, by hand."""
+    """The backward: 64 subnormal quanta times the bound of the other
+    factors, by hand; the forward: 2 quanta."""
     gate_up = np.array([[1.0, -2.0, 30.0, -4.0]])   # G = (1, -2), U = (30, -4)
     r = np.array([0.5])
     go = np.array([[2.0, -1.0]])
     a = subnormal_allowance(gate_up, r, go, 4.0, 25.0)
     tub = np.array([[25.0, 4.0]])                   # min(|U|, 25)
-    np.testing.assert_allclose(a["y"], SUBNORMAL_QUANTA * 0.5 * (tub + 4.0))
+    np.testing.assert_allclose(a["y"], np.full((1, 2), 2 * 2.0 ** -149))   # the forward: 2 quanta flat
     np.testing.assert_allclose(a["dG"], SUBNORMAL_QUANTA * np.array([[2.0, 1.0]]) * 0.5 * (tub + 1.0 + 1.0))
     np.testing.assert_allclose(a["dU"], SUBNORMAL_QUANTA * np.array([[2.0, 1.0]]) * 0.5 * 5.0)
     np.testing.assert_allclose(a["dr"], SUBNORMAL_QUANTA * np.array([2.0 * 29.0 + 1.0 * 8.0]))
-    b = subnormal_allowance(gate_up, r, None, 4.0, None)    # no linear beta: |U| itself
-    np.testing.assert_allclose(b["y"], SUBNORMAL_QUANTA * 0.5 * (np.array([[30.0, 4.0]]) + 4.0))
+    b = subnormal_allowance(gate_up, r, None, 4.0, None)    # no grad_out: the forward's only
+    np.testing.assert_allclose(b["y"], np.full((1, 2), 2 * 2.0 ** -149))
     assert set(b) == {"y"}
