@@ -25,21 +25,25 @@
 //     register, so the activation is applied on the accumulators directly.
 //     Per 16-wide k step a wavefront reads 8 operand fragments from LDS for
 //     16 matrix instructions.
-//   * the hidden axis is consumed in stages of kBK: the x and w rows of a
-//     stage go from global memory straight into LDS (16-byte buffer loads
-//     that write LDS, no register staging), one stage ahead of the one being
-//     multiplied; one barrier per stage.  Rows are not padded:
-//     chunk c (16 bytes) of row R is stored at chunk c ^ f(R), a swizzle
-//     under which the fragment reads of 16 consecutive rows hit distinct
-//     banks.
+//   * the hidden axis is consumed in stages of kBK, two LDS stage buffers,
+//     one barrier per stage.  The x and w rows of a stage come in as 16-byte
+//     buffer loads (16 per thread and stage) into a ring of registers that
+//     holds two stages: during stage kt each slot of stage kt + 1 is written
+//     to the free LDS buffer and at once reloaded with stage kt + 3, so every
+//     load has two stages to land and the loads go out evenly over the
+//     stage.  Rows are not padded: chunk c (16 bytes) of row R is stored at
+//     chunk c ^ f(R), a swizzle under which the fragment reads of 16
+//     consecutive rows hit distinct banks.
 //   * the epilogue stages the bf16 results in LDS and writes whole 16-byte
 //     vectors of each row.
 //
 // MX fp8 operands (E4M3 or E5M2 codes, one E8M0 scale byte per 32 values
 // along the hidden axis): the same tiling with 128 hidden values per 128-byte
 // stage row, two 64-wide k steps of v_mfma_scale_f32_32x32x64_f8f6f4 per
-// stage, each lane giving the scale byte of its row and 32-wide block.  A
-// lane's 32 operand bytes are two 16-byte chunks of the step, taken in an
+// stage, each lane giving the scale byte of its row and 32-wide block; the
+// operands and scale bytes of a stage go from global memory straight into
+// LDS (buffer loads that write LDS) one stage ahead, instead of through the
+// register ring.  A lane's 32 operand bytes are two 16-byte chunks of the step, taken in an
 // order (the same for both operands) under which the instruction's first 32
 // k are exactly the step's first MX block.  The kernel takes the scale bytes
 // stage-major, one dword (the 4 scale bytes of a stage) per row and stage,
@@ -96,14 +100,16 @@ static_assert(kLoads == 2 * kCh, "x and w rows split evenly over the loads");
 constexpr int kBufBytes = kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes;
 constexpr int kGroupM = 16;            // row tiles of a super tile (column tiles not a multiple of 16)
 constexpr int kXcdRows = 8;            // row tiles of an XCD's block in the XCD-aware order (x 4 columns)
-constexpr int kFirstLoads = 8;         // of a stage's 16 loads per thread: issued at the boundary, the rest
-                                       // during the next k step
-constexpr int kLoadSpacing = 2;        // products between consecutive loads
-// fp8 operands (two k steps per stage, each product twice the work): 12 of
-// the loads at the boundary, one per product (measured 5% faster than 8 / 2;
-// bf16 is fastest with 8 / 2)
+// fp8 operands go from global memory straight into LDS (buffer loads that
+// write LDS), one stage ahead: of a stage's 16 loads per thread, 12 at the
+// stage boundary, the rest one per product of the next k step (two k steps
+// per stage, each product twice the work of a bf16 one)
 constexpr int kFirstLoadsF8 = 12;
 constexpr int kLoadSpacingF8 = 1;
+// bf16: register ring slots written to LDS (each followed by its reload) in
+// k steps 0, 1 and 2 of a stage; the slots must be in LDS before the stage's
+// barrier
+constexpr int kRingMoves0 = 6, kRingMoves1 = 11;
 
 using lds_ptr_t = __attribute__((address_space(3))) void *;
 
@@ -381,25 +387,13 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
                 }
             }
     };
-    // Interleave one k step's 16 products with the fragment reads of the
-    // next step: a read between consecutive products keeps LDS requests
-    // flowing while the matrix core works.
-    auto pattern = []() {
-#pragma unroll
-        for (int q = 0; q < kFragReads; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a fragment read
-        }
-        if (kFragReads < 16)
-            __builtin_amdgcn_sched_group_barrier(0x008, 16 - kFragReads, 0);
-    };
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
     Frags f0, f1;
     Scales q0, q1;  // scales of the stage in buffer 0 / buffer 1 (fp8)
-    constexpr int kFirst = F8 ? kFirstLoadsF8 : kFirstLoads, kSpread = F8 ? kLoadSpacingF8 : kLoadSpacing;
-    // k steps 0..kSteps-2 of a stage: products of step st, fragments of step
-    // st + 1 (and the remaining loads of stage kt_next into the other buffer)
+    constexpr int kFirst = kFirstLoadsF8, kSpread = kLoadSpacingF8;
+    // fp8, k step 0 of a stage: its products, fragments of step 1 (and the
+    // remaining loads of stage kt_next into the other buffer)
     auto first_steps = [&](auto buf, int kt_next) {
         const char *s = decltype(buf)::value ? smem1 : smem0;
         const Scales &q = decltype(buf)::value ? q1 : q0;
@@ -414,16 +408,8 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
             if (i < kFragReads)
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        if constexpr (!F8) {
-            read_frags(s, 2, f0);
-            mfmas(f1, q, 1);
-            pattern();
-            read_frags(s, 3, f1);
-            mfmas(f0, q, 2);
-            pattern();
-        }
     };
-    // the stage boundary: once every wavefront has read its last fragments of
+    // fp8, the stage boundary: once every wavefront has read its last fragments of
     // the stage in `buf` and its loads of the next stage (other buffer) have
     // landed, one barrier; then the next stage's first fragments (and
     // scales) and the loads of stage kt_next (into `buf`) go out while the
@@ -449,24 +435,113 @@ situ_glu_grouped_fwd_kernel(const void *__restrict__ x, const void *__restrict__
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- main loop.  Stage kt lives in buffer kt % 2; the loads of stage
-    // kt + 1 are in flight while stage kt is multiplied.  The body is two
+    // ---- main loop.  Stage kt lives in LDS buffer kt % 2.  The body is two
     // stages (one per buffer) with no tail: an odd stage count gets one more
     // stage of zeros (an empty descriptor), which adds nothing.
-    issue_scales(0, Buf0{});
-    issue(0, Buf0{});
-    wait_vmcnt<0>();
-    __syncthreads();
-    read_frags(smem0, 0, f0);
-    if (F8)
-        read_scales(ssc0, q0);
-    issue_scales(1, Buf1{});
-    issue(1, Buf1{}, 0, kFirst);
-    for (int kt = 0; kt < nk; kt += 2) {
-        first_steps(Buf0{}, kt + 1);
-        boundary(Buf0{}, kt + 2);
-        first_steps(Buf1{}, kt + 2);
-        boundary(Buf1{}, kt + 3);
+    if constexpr (F8) {
+        // the loads of stage kt + 1 are in flight into the other buffer while
+        // stage kt is multiplied
+        issue_scales(0, Buf0{});
+        issue(0, Buf0{});
+        wait_vmcnt<0>();
+        __syncthreads();
+        read_frags(smem0, 0, f0);
+        if (F8)
+            read_scales(ssc0, q0);
+        issue_scales(1, Buf1{});
+        issue(1, Buf1{}, 0, kFirst);
+        for (int kt = 0; kt < nk; kt += 2) {
+            first_steps(Buf0{}, kt + 1);
+            boundary(Buf0{}, kt + 2);
+            first_steps(Buf1{}, kt + 2);
+            boundary(Buf1{}, kt + 3);
+        }
+    } else {
+        // register ring: ring0 / ring1 hold the even / odd stages in flight,
+        // slot j of a stage = load j of this thread
+        u32x4 ring0[kLoads], ring1[kLoads];
+        auto gload = [&](int kt, int j) -> u32x4 {
+            const rsrc_t r = kt >= nk ? rz : j < kCh ? ra : (j - kCh < kCh / 2 ? rg : ru);
+            return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff[j % kCh], (int)((uint32_t)kt * kRowB), 0);
+        };
+        // slot j lands where the direct-to-LDS load j would write: 1 KiB block
+        // 4 j + wv, 16 bytes per lane
+        auto lwrite = [&](char *base, int j, const u32x4 &v) {
+            *reinterpret_cast<u32x4 *>(base + (4 * j + wv) * 1024 + lane * 16) = v;
+        };
+        // a barrier that waits for this wavefront's LDS operations only (the
+        // ring's global loads stay in flight); the empty asm statements keep
+        // the compiler from moving LDS accesses across it
+        auto lds_barrier = []() {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // slots j0..j1-1 of ring R: write to LDS buffer ns, then reload with stage kt_load
+        auto move = [&](auto &R, char *ns, int kt_load, int j0, int j1) {
+#pragma unroll
+            for (int j = j0; j < j1; ++j) {
+                lwrite(ns, j, R[j]);
+                R[j] = gload(kt_load, j);
+            }
+        };
+        // a k step's order: a product, then a fragment read (first nr
+        // products), and after every second product one slot write + reload
+        // (first nw)
+        auto steps = [](int nr, int nw) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < nr)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i % 2 == 1 && i / 2 < nw) {
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+        };
+        const Scales qn{};  // unused by bf16 products
+        // stage kt from buffer `buf`: its four k steps; stage kt + 1 moves from
+        // ring R into the other buffer and R refills with stage kt + 3
+        auto stage = [&](auto buf, auto &R, int kt) {
+            constexpr int b = decltype(buf)::value;
+            const char *s = b ? smem1 : smem0;
+            char *ns = b ? smem0 : smem1;
+            read_frags(s, 1, f1);
+            move(R, ns, kt + 3, 0, kRingMoves0);
+            mfmas(f0, qn, 0);
+            steps(kFragReads, kRingMoves0);
+            read_frags(s, 2, f0);
+            move(R, ns, kt + 3, kRingMoves0, kRingMoves1);
+            mfmas(f1, qn, 1);
+            steps(kFragReads, kRingMoves1 - kRingMoves0);
+            read_frags(s, 3, f1);
+            move(R, ns, kt + 3, kRingMoves1, kLoads);
+            mfmas(f0, qn, 2);
+            steps(kFragReads, kLoads - kRingMoves1);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+            // the last k step's products run while the next stage's first
+            // fragments are read
+            read_frags(ns, 0, f0);
+            mfmas(f1, qn, 3);
+            steps(kFragReads, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            ring0[j] = gload(0, j);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            ring1[j] = gload(1, j);
+        move(ring0, smem0, 2, 0, kLoads);
+        lds_barrier();
+        read_frags(smem0, 0, f0);
+        for (int kt = 0; kt < nk; kt += 2) {
+            stage(Buf0{}, ring1, kt);
+            stage(Buf1{}, ring0, kt + 1);
+        }
     }
     wait_vmcnt<0>();  // loads past the last stage (zeros) have landed
     __syncthreads();  // every wavefront is done with the stage buffers
