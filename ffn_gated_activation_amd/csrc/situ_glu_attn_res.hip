@@ -265,8 +265,8 @@ situ_glu_attn_res_vec_kernel(const void *__restrict__ blocks, const void *__rest
 // block v for v < 16, dot products of block v - 16 above) of row q of
 // wavefront w at part[v * kRowStride + 4 w + q].  The cross-row and
 // cross-wavefront sums are left to the softmax step, which reads each
-// value's 4 * nwaves partials as 16-byte vectors (the stride is padded so
-// that the 32 reading lanes fall in distinct banks).  Compared with full
+// value's 4 * nwaves partials as 16-byte vectors, two lanes per value (the
+// stride is padded by 16 bytes against bank conflicts).  Compared with full
 // wavefront sums this saves four lane reads and three adds per sum.
 constexpr int kRowStride = 4 * kMaxWaves + 4;
 constexpr int kRowPartFloats = 2 * kAresMaxBlocks * kRowStride;
@@ -291,20 +291,31 @@ __device__ __forceinline__ void block_row_partials(float ss, float d, int b, flo
     }
 }
 
-// Softmax over MAXNB blocks of which the first nb are real (straight-line:
-// blocks past nb get probability 0), from the row partials: lane v (< 32)
-// adds value v's partials in a fixed order (four running sums over the
-// wavefronts, then pairwise).  P ends in scalar registers.
+// Softmax over MAXNB blocks of which the first nb are real (blocks past nb
+// get probability 0), from the row partials, spread over the wavefront
+// instead of repeated per block in every lane: block b owns lanes 4b..4b+3.
+// Lanes 4b and 4b+1 add the first and the second half of the wavefronts'
+// partials of the block's sum of squares, lanes 4b+2 and 4b+3 those of its
+// dot product (fixed order: four running sums, then pairwise); a quad
+// exchange puts both sums on every lane of the quad, so each quad holds its
+// block's logit.  Largest logit and denominator: two DPP steps inside each
+// 16-lane row (4 blocks), then the rows' values in row order.  P ends in
+// scalar registers.
 template <int MAXNB>
-__device__ __forceinline__ void block_probs_rows(const float *part, int nwaves, int nb, float inv_h, float eps,
-                                                 float *P)
+__device__ __forceinline__ void block_probs_quads(const float *part, int nwaves, int nb, float inv_h, float eps,
+                                                  float *P)
 {
+    static_assert(4 * MAXNB <= 64, "one quad of lanes per block");
+    constexpr int kRows = (MAXNB + 3) / 4;
     const int lane = threadIdx.x & 63;
+    const int b = lane >> 2, h = lane & 3;
+    const int half = (nwaves + 1) >> 1;
     float tot = 0.0f;
-    if (lane < 2 * kAresMaxBlocks) {
-        const float4 *pv = reinterpret_cast<const float4 *>(part + lane * kRowStride);
+    if (b < MAXNB) {
+        const float4 *pv = reinterpret_cast<const float4 *>(part + ((h >> 1) * kAresMaxBlocks + b) * kRowStride);
+        const int w1 = (h & 1) ? nwaves : half;
         float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-        for (int w = 0; w < nwaves; ++w) {
+        for (int w = (h & 1) ? half : 0; w < w1; ++w) {
             const float4 v = pv[w];
             a0 += v.x;
             a1 += v.y;
@@ -313,25 +324,27 @@ __device__ __forceinline__ void block_probs_rows(const float *part, int nwaves, 
         }
         tot = (a0 + a1) + (a2 + a3);
     }
-    float l[MAXNB];
-    float lmax = -__builtin_inff();
+    tot += dpp_f<0xB1>(tot);              // quad_perm [1,0,3,2]: the two halves
+    const float ss = dpp_f<0x00>(tot);    // quad_perm [0,0,0,0]: sum of squares
+    const float dd = dpp_f<0xAA>(tot);    // quad_perm [2,2,2,2]: dot product
+    const float l = b < nb ? dd * __builtin_amdgcn_rsqf(fmaf(ss, inv_h, eps)) : -__builtin_inff();
+    float m = fmaxf(l, dpp_f<0x141>(l));  // row_half_mirror: quads 0 <-> 1, 2 <-> 3
+    m = fmaxf(m, dpp_f<0x140>(m));        // row_mirror: the two half rows
+    float lmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
 #pragma unroll
-    for (int b = 0; b < MAXNB; ++b) {
-        const float ss = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), b));
-        const float dd = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), kAresMaxBlocks + b));
-        l[b] = b < nb ? dd * __builtin_amdgcn_rsqf(fmaf(ss, inv_h, eps)) : -__builtin_inff();
-        lmax = fmaxf(lmax, l[b]);
-    }
-    float den = 0.0f;
+    for (int q = 1; q < kRows; ++q)
+        lmax = fmaxf(lmax, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16 * q)));
+    const float e = __builtin_amdgcn_exp2f((l - lmax) * kLog2e);
+    float t = e + dpp_f<0x141>(e);
+    t += dpp_f<0x140>(t);
+    float den = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 0));
 #pragma unroll
-    for (int b = 0; b < MAXNB; ++b) {
-        l[b] = __builtin_amdgcn_exp2f((l[b] - lmax) * kLog2e);
-        den += l[b];
-    }
-    const float inv = 1.0f / den;
+    for (int q = 1; q < kRows; ++q)
+        den += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 16 * q));
+    const float pe = e * (1.0f / den);
 #pragma unroll
-    for (int b = 0; b < MAXNB; ++b)
-        P[b] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(l[b] * inv)));
+    for (int k = 0; k < MAXNB; ++k)
+        P[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), 4 * k));
 }
 
 // Streaming variant of the 128-bit path for up to MAXNB blocks: one
@@ -390,7 +403,7 @@ __device__ __forceinline__ void ares_mix_token(const uint4 *xv, const float *c, 
     // above the barrier, every block's fp32 copy would be live at once
     __builtin_amdgcn_sched_barrier(0);
     float P[MAXNB];
-    block_probs_rows<MAXNB>(part, nwaves, nb, 1.0f / (float)hidden, eps, P);
+    block_probs_quads<MAXNB>(part, nwaves, nb, 1.0f / (float)hidden, eps, P);
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
