@@ -322,7 +322,10 @@ int env_override(const char *name, int lo, int hi)
 constexpr int kDrWavesPerBlock = 4;  // row mapping: target wavefronts per workgroup
 constexpr int kMaxRowWaves = 16;     // row mapping: wavefronts per row at most
 
-int plan_split(int64_t rows, int64_t inter, int64_t es, bool bwd, bool lb, bool row_dr, situ::ChunkSplit &sp)
+// group4: the MXFP8 forward, where a wavefront that takes a row's aligned
+// group of four chunks writes their scale bytes with one store
+int plan_split(int64_t rows, int64_t inter, int64_t es, bool bwd, bool lb, bool row_dr, situ::ChunkSplit &sp,
+               bool group4 = false)
 {
     static const int env_k = env_override("SITU_GLU_CHUNKS_PER_WAVE", 1, 8);
     static const int env_w = env_override("SITU_GLU_WAVES_PER_BLOCK", 1, 4);
@@ -343,7 +346,7 @@ int plan_split(int64_t rows, int64_t inter, int64_t es, bool bwd, bool lb, bool 
         g.magic = (uint32_t)((((uint64_t)1) << (31 + l)) / (uint64_t)cpr + 1);
         g.shift = l - 1;
     }
-    int k = es == 2 ? (lb ? 2 : 1) : 2;
+    int k = es == 2 ? (group4 && cpr % 4 == 0 ? 4 : lb ? 2 : 1) : 2;
     int wpb = es == 2 && bwd && lb ? 4 : 1;
     if (env_k)
         k = env_k;
@@ -435,8 +438,8 @@ int situ_glu_split(int io_dtype, int64_t rows, int64_t intermediate, int linear_
     g_last_error.clear();
     if (!dtype_ok(io_dtype))
         return fail(SITU_ERR_INVALID_ARG, "io_dtype %d is not SITU_DTYPE_F32 (0) or SITU_DTYPE_BF16 (1)", io_dtype);
-    if (direction < 0 || direction > 2)
-        return fail(SITU_ERR_INVALID_ARG, "direction %d is not 0, 1 or 2", direction);
+    if (direction < 0 || direction > 3)
+        return fail(SITU_ERR_INVALID_ARG, "direction %d is not 0, 1, 2 or 3", direction);
     if (!out)
         return fail(SITU_ERR_INVALID_ARG, "out is NULL");
     if (rows < 1 || rows > (int64_t)0x7fffffff || intermediate < 1 || intermediate > (int64_t)0x3fffffff)
@@ -446,7 +449,8 @@ int situ_glu_split(int io_dtype, int64_t rows, int64_t intermediate, int linear_
     if ((intermediate * es) % 16 || intermediate * 2 * es >= ((int64_t)1 << 31))
         return fail(SITU_ERR_INVALID_ARG, "these sizes take the element path (no chunk split)");
     situ::ChunkSplit sp{};
-    const int rc = plan_split(rows, intermediate, es, direction > 0, linear_beta_given != 0, direction == 2, sp);
+    const int rc = plan_split(rows, intermediate, es, direction == 1 || direction == 2, linear_beta_given != 0,
+                              direction == 2, sp, direction == 3);
     if (rc)
         return rc;
     out[0] = sp.geom.cpr;
@@ -675,7 +679,7 @@ int situ_glu_fwd_mxfp8(const void *gate_up, int io_dtype, int64_t rows, int64_t 
     L.fmt = fp8_format == SITU_FP8_E5M2 ? situ::FP8_E5M2 : situ::FP8_E4M3;
     L.ceil_mode = scale_mode == SITU_MX_SCALE_CEIL;
     L.rows_per_block = rows_per_block_override();
-    if (L.vec && (rc = plan_split(rows, intermediate, es, false, L.lb, false, L.split)))
+    if (L.vec && (rc = plan_split(rows, intermediate, es, false, L.lb, false, L.split, true)))
         return rc;
     L.gk = gate_consts(beta);
     L.uk = situ::make_up_consts(linear_beta ? *linear_beta : 1.0);

@@ -156,14 +156,10 @@ __device__ __forceinline__ uint32_t group_max(uint32_t m)
 }
 
 // One lane's vector of E values (vector index v of its row): block maximum,
-// scale, codes.  Codes go to byte offset v * E of the row's code buffer, the
-// scale (from the first lane of the block) to byte v / (32 / E) of the row's
-// scale buffer; both buffers drop stores past their end.  Every lane issues
-// the scale store, the block's other lanes at an offset past any buffer's
-// end: no lane mask to set up and restore around it (measured 3% faster for
-// the fused forward than a store under `if (first lane)`).
+// scale code, element codes.  Codes go to byte offset v * E of the row's
+// code buffer (stores past its end are dropped); the scale code is returned.
 template <int FMT, int MODE, int E>
-__device__ __forceinline__ void quantize_vector(const float *y, int v, int lane, rsrc_t rc, rsrc_t rs)
+__device__ __forceinline__ uint32_t quantize_codes(const float *y, int v, rsrc_t rc)
 {
     constexpr int kLanes = kMxBlock / E;
     const uint32_t m = group_max<kLanes>(lane_amax_bits<E>(y));
@@ -174,6 +170,19 @@ __device__ __forceinline__ void quantize_vector(const float *y, int v, int lane,
     } else {
         __builtin_amdgcn_raw_buffer_store_b32(encode4<FMT, MODE>(y, code), rc, v * 4, 0, kStreaming);
     }
+    return code;
+}
+
+// The same with the scale stored: from the first lane of the block to byte
+// v / (32 / E) of the row's scale buffer (dropped past its end).  Every lane
+// issues the scale store, the block's other lanes at an offset past any
+// buffer's end: no lane mask to set up and restore around it (measured 3%
+// faster for the fused forward than a store under `if (first lane)`).
+template <int FMT, int MODE, int E>
+__device__ __forceinline__ void quantize_vector(const float *y, int v, int lane, rsrc_t rc, rsrc_t rs)
+{
+    constexpr int kLanes = kMxBlock / E;
+    const uint32_t code = quantize_codes<FMT, MODE, E>(y, v, rc);
     __builtin_amdgcn_raw_buffer_store_b8((unsigned char)code, rs,
                                          (lane & (kLanes - 1)) == 0 ? v / kLanes : 0x7fffffff, 0, kStreaming);
 }
@@ -218,10 +227,11 @@ __device__ __forceinline__ Chunk<2, 2> mx_chunk_at(int64_t row, uint32_t c, bool
 // io with a linear beta takes the polynomial up branch when the wavefront's
 // |U| allow it (degree 7: the fp32 Y stays inside the chain's 1e-5).  Past
 // the row end the loads returned zeros: Y = 0 there, which leaves every
-// block maximum unchanged, and the stores are dropped.
-template <int IO, bool LB, bool FAST, bool RWB, int FMT, int MODE>
-__device__ __forceinline__ void fwd_mx_chunk(const uint4 *v, const Chunk<2, 2> &k, int lane, const GateK &gk,
-                                             const UpK &uk)
+// block maximum unchanged, and the stores are dropped.  KEEP: the block's
+// scale code is returned instead of stored (the caller stores a group's).
+template <int IO, bool LB, bool FAST, bool RWB, int FMT, int MODE, bool KEEP = false>
+__device__ __forceinline__ uint32_t fwd_mx_chunk(const uint4 *v, const Chunk<2, 2> &k, int lane, const GateK &gk,
+                                                 const UpK &uk)
 {
     using T = Io<IO>;
     constexpr int E = T::kPerVec;
@@ -239,8 +249,13 @@ __device__ __forceinline__ void fwd_mx_chunk(const uint4 *v, const Chunk<2, 2> &
         for (int e = 0; e < E; ++e)
             y[e] = fwd_elem<LB, FAST, IO == IO_F32>(g[e], u[e], rscale, gk, uk);
     }
-    quantize_vector<FMT, MODE, E>(y, lane, lane, k.out[0], k.out[1]);
+    uint32_t code = 0;
+    if (KEEP)
+        code = quantize_codes<FMT, MODE, E>(y, lane, k.out[0]);
+    else
+        quantize_vector<FMT, MODE, E>(y, lane, lane, k.out[0], k.out[1]);
     order_fence();
+    return code;
 }
 
 // Fused forward, 128-bit path: flat chunk mapping, wavefront w takes chunks
@@ -269,6 +284,32 @@ situ_glu_fwd_mx_kernel(const void *__restrict__ gate_up, const void *__restrict_
         }
     };
     const char *gp = static_cast<const char *>(gate_up);
+    if (IO == IO_BF16 && g.k == 4 && g.cpr % 4 == 0) {
+        // the wavefront's four chunks are one aligned group of a row: lane
+        // 4q + j keeps block q's scale code of chunk j, and one byte store
+        // writes the group's 64 scale bytes (chunk j's block q at 16 j + q)
+        const uint32_t j = lane & 3, q = lane >> 2;
+        uint4 A[2], B[2];
+        Chunk<2, 2> ka = mx_chunk_at<IO>(row, c, true, g, gp, codes, scales, inter, nblk,
+                                         weight_bits<RWB>(rw, row * rw_stride));
+        load_chunk(A, ka, voff);
+        Chunk<2, 2> kb = mx_chunk_at<IO>(row, c + 1, true, g, gp, codes, scales, inter, nblk, ka.rbits);
+        load_chunk(B, kb, voff);
+        uint32_t sc = fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE, true>(A, ka, lane, gk, uk);
+        ka = mx_chunk_at<IO>(row, c + 2, true, g, gp, codes, scales, inter, nblk, kb.rbits);
+        load_chunk(A, ka, voff);
+        const uint32_t s1 = fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE, true>(B, kb, lane, gk, uk);
+        sc = j == 1 ? s1 : sc;
+        kb = mx_chunk_at<IO>(row, c + 3, true, g, gp, codes, scales, inter, nblk, ka.rbits);
+        load_chunk(B, kb, voff);
+        const uint32_t s2 = fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE, true>(A, ka, lane, gk, uk);
+        sc = j == 2 ? s2 : sc;
+        const uint32_t s3 = fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE, true>(B, kb, lane, gk, uk);
+        sc = j == 3 ? s3 : sc;
+        const rsrc_t rs = make_rsrc(scales + row * (int64_t)nblk + c * (kChunkBytes / 2 / kMxBlock), 64u);
+        __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, (int)(16 * j + q), 0, kStreaming);
+        return;
+    }
 #define SITU_MX_BODY(R, K) fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE>(R, K, lane, gk, uk)
 #define SITU_MAKE(R, C, L) \
     mx_chunk_at<IO>(R, C, L, g, gp, codes, scales, inter, nblk, weight_bits<RWB>(rw, (R) * rw_stride))

@@ -421,7 +421,8 @@ def situ_glu_last_error() -> str:
 def situ_glu_split(io_dtype: torch.dtype, rows: int, intermediate: int, linear_beta_given: bool,
                    direction: int) -> dict:
     """The 128-bit path's work split for a call with these sizes (host only):
-    direction 0 forward, 1 backward, 2 backward with d_routing_weights."""
+    direction 0 forward, 1 backward, 2 backward with d_routing_weights, 3 the
+    MXFP8 forward."""
     import ctypes
     lib = _capi.load()
     out = (ctypes.c_int64 * 10)()

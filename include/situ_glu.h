@@ -475,7 +475,9 @@ int situ_glu_gate_window(double beta, float *out);
 /*
  * Diagnostic: the work split of the 128-bit path for a call with these sizes
  * (host only, no device work).  direction: 0 situ_glu_fwd, 1 situ_glu_bwd
- * without d_routing_weights, 2 with it.  A chunk is 64 lanes x 16 bytes
+ * without d_routing_weights, 2 with it, 3 situ_glu_fwd_mxfp8 (bf16 with
+ * chunks per row a multiple of 4: four chunks per wavefront, an aligned
+ * group of one row, whose scale bytes leave in one store).  A chunk is 64 lanes x 16 bytes
  * (1 KiB) of each half row; out must hold 10 int64:
  *   out[0] chunks per row, out[1] chunks of the tensor, out[2] chunks per
  *   wavefront, out[3] wavefronts per row (direction 2; else 0: chunks are

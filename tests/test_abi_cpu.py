@@ -524,7 +524,8 @@ def test_split_covers_every_chunk(lib, capi):
     workloads' shapes and for sampled indices up to 2^31 at many other
     divisors; the flat grid covers every chunk once; the row mapping gives
     each row at most 16 wavefronts that cover its chunks, and the slot
-    division is exact for every slot of a workgroup."""
+    division is exact for every slot of a workgroup; the MXFP8 forward gives
+    a wavefront a row's aligned group of four chunks where it can."""
     out = (ctypes.c_int64 * 10)()
     rng = np.random.default_rng(0)
     shapes = [(256, 512, capi.SITU_DTYPE_F32), (8192, 2048, capi.SITU_DTYPE_BF16),
@@ -535,7 +536,7 @@ def test_split_covers_every_chunk(lib, capi):
     for rows, inter, dt in shapes:
         es = 4 if dt == capi.SITU_DTYPE_F32 else 2
         for lbg in (0, 1):
-            for direction in (0, 1, 2):
+            for direction in (0, 1, 2, 3):
                 assert lib.situ_glu_split(dt, rows, inter, lbg, direction, out) == 0, capi.last_error(lib)
                 cpr, total, k, wpr, grid, block, magic, shift, wmagic, half = [int(v) for v in out]
                 assert half == inter * es and cpr == -(-half // 1024) and total == rows * cpr
@@ -545,7 +546,10 @@ def test_split_covers_every_chunk(lib, capi):
                     q = (x * np.uint64(magic)) >> np.uint64(32 + shift)
                     assert np.array_equal(q, x // np.uint64(cpr)), (rows, inter, direction)
                 assert 64 <= block <= 1024 and block % 64 == 0
-                if direction < 2:
+                if direction == 3 and es == 2 and cpr % 4 == 0:
+                    # a wavefront's four chunks are one aligned group of a row
+                    assert k == 4 and total % 4 == 0
+                if direction != 2:
                     assert wpr == 0 and block <= 256
                     waves = grid * (block // 64)
                     assert waves * k >= total and (waves - block // 64) * k < total
@@ -569,7 +573,7 @@ def test_split_covers_every_chunk(lib, capi):
         assert np.array_equal(q, x // np.uint64(cpr)), cpr
     # rejected: element-path sizes, bad direction, too many chunks
     assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 12, 1, 0, out) == capi.SITU_ERR_INVALID_ARG
-    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 16, 1, 3, out) == capi.SITU_ERR_INVALID_ARG
+    assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 16, 1, 4, out) == capi.SITU_ERR_INVALID_ARG
     assert lib.situ_glu_split(7, 4, 16, 1, 0, out) == capi.SITU_ERR_INVALID_ARG
     assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, 4, 16, 1, 0, None) == capi.SITU_ERR_INVALID_ARG
     assert lib.situ_glu_split(capi.SITU_DTYPE_BF16, (1 << 31) - 1, 1024, 1, 0, out) == capi.SITU_ERR_UNSUPPORTED
