@@ -306,7 +306,10 @@ situ_glu_fwd_mx_kernel(const void *__restrict__ gate_up, const void *__restrict_
         sc = j == 2 ? s2 : sc;
         const uint32_t s3 = fwd_mx_chunk<IO, LB, FAST, RWB, FMT, MODE, true>(B, kb, lane, gk, uk);
         sc = j == 3 ? s3 : sc;
-        const rsrc_t rs = make_rsrc(scales + row * (int64_t)nblk + c * (kChunkBytes / 2 / kMxBlock), 64u);
+        // the row's blocks from the group's first on, at most 64: the last
+        // chunk of a row may be partial, and bytes past the row are dropped
+        const uint32_t b0 = c * (kChunkBytes / 2 / kMxBlock);
+        const rsrc_t rs = make_rsrc(scales + row * (int64_t)nblk + b0, nblk - b0 < 64u ? nblk - b0 : 64u);
         __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sc, rs, (int)(16 * j + q), 0, kStreaming);
         return;
     }

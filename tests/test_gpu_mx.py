@@ -196,6 +196,8 @@ SMALL = [
     ("routed_top8", 8, 1000),     # 128-bit path, ragged strip
     ("fp32_small", 9, 1003),      # element path
     ("routed_top8", 8, 40000),    # several strips per wavefront
+    ("routed_top8", 8, 1800),     # four chunks per row, the last one partial (57 blocks)
+    ("stress_sat", 3, 3848),      # two groups of four chunks per row, the last chunk partial
 ]
 
 
