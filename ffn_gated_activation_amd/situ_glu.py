@@ -33,6 +33,15 @@ def _check_device(*ts):
             raise ValueError("situ_glu runs on the GPU only: every tensor must be on a cuda device")
 
 
+def _refuse_grad(name: str, *ts, hint: str = ""):
+    """The forward-only entry points have no backward: refuse inputs that
+    would need one (grad mode on and a tensor requiring grad) instead of
+    returning an output detached from the graph."""
+    if torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in ts):
+        raise RuntimeError(f"{name} has no backward: call it on tensors that do not require grad, or under "
+                           f"torch.no_grad(){hint}")
+
+
 def _flatten(gate_up: torch.Tensor, routing_weights: torch.Tensor):
     if gate_up.dim() < 1 or gate_up.shape[-1] % 2:
         raise ValueError(f"gate_up must be [..., 2*intermediate], got {tuple(gate_up.shape)}")
@@ -69,6 +78,8 @@ def situ_glu_fwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, beta: flo
     routing_weights [..., 1] row aligned, or one weight.  Returns [..., I] in
     gate_up's dtype.
     """
+    _refuse_grad("situ_glu_fwd", gate_up, routing_weights,
+                 hint="; ffn_gated_activation_amd.weighted_situ is the differentiable form")
     lib = _capi.load()
     _check_device(gate_up, routing_weights, out)
     io = _io_dtype(gate_up, "gate_up")
@@ -161,6 +172,7 @@ def situ_glu_fwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, bet
     ``codes.view(torch.float8_e4m3fn)`` (or ``float8_e5m2``) gives the
     elements; the value of element j is element * 2^(scales[..., j // 32] - 127).
     """
+    _refuse_grad("situ_glu_fwd_mxfp8", gate_up, routing_weights)
     lib = _capi.load()
     _check_device(gate_up, routing_weights, codes, scales)
     io = _io_dtype(gate_up, "gate_up")
@@ -226,6 +238,7 @@ def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: 
                          codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """MXFP8 block quantisation of x [..., cols] (float32 or bfloat16) along its
     last axis: returns (codes uint8 [..., cols], scales uint8 [..., ceil(cols / 32)])."""
+    _refuse_grad("situ_glu_mx_quantize", x)
     lib = _capi.load()
     _check_device(x, codes, scales)
     io = _io_dtype(x, "x")
@@ -253,6 +266,7 @@ def situ_glu_attn_res_fwd(blocks: torch.Tensor | None, prefix: torch.Tensor | No
     norm_weight, epsilon eps), projection to one logit per block
     (proj_weight), softmax over the blocks, and the weighted sum of the raw
     values.  Returns [T, H] in out_dtype (default: the values' dtype)."""
+    _refuse_grad("situ_glu_attn_res_fwd", blocks, prefix, norm_weight, proj_weight)
     lib = _capi.load()
     _check_device(blocks, prefix, norm_weight, proj_weight, out)
     ref = blocks if blocks is not None else prefix
@@ -338,6 +352,7 @@ def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: t
     device (expert e owns rows group_offsets[e] .. group_offsets[e+1]),
     routing_weights [M] / [M, 1] or one weight.  Returns out [M, I] bf16, or
     (out, gate_up [M, 2I] bf16) when want_gate_up."""
+    _refuse_grad("situ_glu_grouped_fwd", x, weight, routing_weights)
     lib = _capi.load()
     _check_device(x, weight, group_offsets, routing_weights, out, gate_up_out)
     if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
@@ -374,6 +389,7 @@ def situ_glu_grouped_fwd_mxfp8(x_codes: torch.Tensor, x_scales: torch.Tensor, we
     decode(code) * 2^(scale[k / 32] - 127).  workspace: a device buffer of at
     least situ_glu_grouped_fwd_mxfp8_workspace_bytes(...) bytes (allocated
     here when not given).  The rest is as for situ_glu_grouped_fwd."""
+    _refuse_grad("situ_glu_grouped_fwd_mxfp8", routing_weights)
     lib = _capi.load()
     fmt = _mx_args(fp8_format, "floor")[0]
     _check_device(x_codes, x_scales, weight_codes, weight_scales, group_offsets, routing_weights, out, gate_up_out)

@@ -453,6 +453,36 @@ def test_python_layer_rejects_cpu_tensors():
         situ_glu_fwd(torch.zeros(2, 8), torch.ones(2, 1))
 
 
+def test_forward_only_entry_points_refuse_grad():
+    """The entry points without a backward refuse tensors that need one
+    (grad mode on, an input requiring grad) rather than returning an output
+    cut off from the graph; under no_grad they go on to the device check."""
+    import torch
+
+    import ffn_gated_activation_amd as m
+    gu = torch.zeros(2, 64, requires_grad=True)
+    rw = torch.ones(2, 1)
+    calls = [
+        lambda: m.situ_glu_fwd(gu, rw),
+        lambda: m.situ_glu_fwd_mxfp8(gu, rw),
+        lambda: m.situ_glu_mx_quantize(gu),
+        lambda: m.situ_glu_attn_res_fwd(torch.zeros(2, 3, 64), None, gu[0], torch.ones(64), 1e-6),
+        lambda: m.situ_glu_grouped_fwd(torch.zeros(4, 64), torch.zeros(1, 128, 64), torch.tensor([0, 4]),
+                                       torch.ones(4, 1, requires_grad=True)),
+        lambda: m.situ_glu_grouped_fwd_mxfp8(None, None, None, None, torch.tensor([0, 4]),
+                                             torch.ones(4, 1, requires_grad=True)),
+    ]
+    for call in calls:
+        with pytest.raises(RuntimeError, match="has no backward"):
+            call()
+    with torch.no_grad():
+        with pytest.raises(ValueError, match="GPU only"):
+            m.situ_glu_fwd(gu, rw)
+    # the differentiable form is weighted_situ (its forward runs with grad mode off inside autograd)
+    with pytest.raises(ValueError, match="GPU only"):
+        m.weighted_situ(gu, rw)
+
+
 def _bf16_neighbours(x: float, n: int) -> np.ndarray:
     """The 2n+1 bf16 values around the bf16 value x (bit patterns +-n)."""
     b = int(np.float32(x).view(np.uint32)) >> 16
