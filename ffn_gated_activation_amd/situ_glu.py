@@ -13,6 +13,8 @@ broadcast over all rows).
 """
 from __future__ import annotations
 
+import functools
+
 import torch
 
 from . import _capi
@@ -28,9 +30,29 @@ def _io_dtype(t: torch.Tensor, what: str) -> int:
 
 
 def _check_device(*ts):
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("situ_glu runs on the GPU only: every tensor must be on a cuda device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"every tensor of one call must be on the same device ({dev} and {t.device})")
+
+
+def _on_tensor_device(fn):
+    """Run an entry point with its tensors' GPU as the current device, so that
+    the launch goes to that device and to its current stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        for a in list(args) + list(kwargs.values()):
+            if isinstance(a, torch.Tensor) and a.is_cuda:
+                with torch.cuda.device(a.device):
+                    return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+    return wrapper
 
 
 def _refuse_grad(name: str, *ts, hint: str = ""):
@@ -70,6 +92,7 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+@_on_tensor_device
 def situ_glu_fwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, beta: float = 4.0,
                  linear_beta: float | None = 25.0, out: torch.Tensor | None = None) -> torch.Tensor:
     """Y = r * (beta tanh(G/beta) sigmoid(G)) * (linear_beta tanh(U/linear_beta) or U).
@@ -99,6 +122,7 @@ def situ_glu_bwd_workspace_bytes(rows: int, intermediate: int, rw_rows: int) -> 
     return int(_capi.load().situ_glu_bwd_workspace_bytes(rows, intermediate, rw_rows))
 
 
+@_on_tensor_device
 def situ_glu_bwd(gate_up: torch.Tensor, routing_weights: torch.Tensor, grad_out: torch.Tensor,
                  beta: float = 4.0, linear_beta: float | None = 25.0, want_drw: bool = True,
                  d_gate_up: torch.Tensor | None = None, d_routing_weights: torch.Tensor | None = None,
@@ -163,6 +187,7 @@ def _mx_outputs(lead, cols, device, codes, scales):
     return codes, scales
 
 
+@_on_tensor_device
 def situ_glu_fwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, beta: float = 4.0,
                        linear_beta: float | None = 25.0, fp8_format: str = "e4m3", scale_mode: str = "floor",
                        codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
@@ -186,6 +211,7 @@ def situ_glu_fwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, bet
     return codes, scales
 
 
+@_on_tensor_device
 def situ_glu_bwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, grad_out: torch.Tensor,
                        beta: float = 4.0, linear_beta: float | None = 25.0, want_drw: bool = True,
                        fp8_format: str = "e4m3", scale_mode: str = "floor", d_codes: torch.Tensor | None = None,
@@ -234,6 +260,7 @@ def situ_glu_bwd_mxfp8(gate_up: torch.Tensor, routing_weights: torch.Tensor, gra
     return d_codes, d_scales, d_routing_weights
 
 
+@_on_tensor_device
 def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: str = "floor",
                          codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """MXFP8 block quantisation of x [..., cols] (float32 or bfloat16) along its
@@ -258,6 +285,7 @@ def situ_glu_mx_quantize(x: torch.Tensor, fp8_format: str = "e4m3", scale_mode: 
     return codes, scales
 
 
+@_on_tensor_device
 def situ_glu_attn_res_fwd(blocks: torch.Tensor | None, prefix: torch.Tensor | None, norm_weight: torch.Tensor,
                           proj_weight: torch.Tensor, eps: float, out_dtype: torch.dtype | None = None,
                           out: torch.Tensor | None = None) -> torch.Tensor:
@@ -341,6 +369,7 @@ def _grouped_outputs(rows, experts, two_i, group_offsets, routing_weights, out, 
     return rwd, rw_rows, out, gate_up_out
 
 
+@_on_tensor_device
 def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: torch.Tensor,
                          routing_weights: torch.Tensor, beta: float = 4.0, linear_beta: float | None = 25.0,
                          want_gate_up: bool = False, out: torch.Tensor | None = None,
@@ -375,6 +404,7 @@ def situ_glu_grouped_fwd(x: torch.Tensor, weight: torch.Tensor, group_offsets: t
 _FP8_CODE_DTYPES = {"e4m3": (torch.uint8, torch.float8_e4m3fn), "e5m2": (torch.uint8, torch.float8_e5m2)}
 
 
+@_on_tensor_device
 def situ_glu_grouped_fwd_mxfp8(x_codes: torch.Tensor, x_scales: torch.Tensor, weight_codes: torch.Tensor,
                                weight_scales: torch.Tensor, group_offsets: torch.Tensor,
                                routing_weights: torch.Tensor, fp8_format: str = "e4m3", beta: float = 4.0,

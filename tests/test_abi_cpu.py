@@ -453,6 +453,22 @@ def test_python_layer_rejects_cpu_tensors():
         situ_glu_fwd(torch.zeros(2, 8), torch.ones(2, 1))
 
 
+def test_tensors_of_one_call_share_a_device():
+    """Every tensor of a call must sit on one GPU (the call then runs with that
+    GPU current); checked on stand-ins, as the CPU has no GPU tensors."""
+    from ffn_gated_activation_amd.situ_glu import _check_device
+
+    class OnGpu:
+        is_cuda = True
+
+        def __init__(self, dev):
+            self.device = dev
+
+    _check_device(OnGpu("cuda:0"), None, OnGpu("cuda:0"))
+    with pytest.raises(ValueError, match="same device"):
+        _check_device(OnGpu("cuda:0"), OnGpu("cuda:1"))
+
+
 def test_forward_only_entry_points_refuse_grad():
     """The entry points without a backward refuse tensors that need one
     (grad mode on, an input requiring grad) rather than returning an output
