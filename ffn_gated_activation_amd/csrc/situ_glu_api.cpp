@@ -313,10 +313,12 @@ int env_override(const char *name, int lo, int hi)
 // Work split of the 128-bit path (chunks of 1 KiB of every stream; see
 // situ::ChunkGeom).  Measured on MI355X with bf16 io: single-wavefront
 // workgroups of one chunk each read and write at 6.5-6.8 TB/s, the copy
-// ceiling of that pattern; with a linear beta the up branch's arithmetic
-// needs two chunks per wavefront (the second one's loads in flight during the
-// first one's math), and the backward four wavefronts per workgroup.  Longer
-// chunk runs per wavefront and persistent grid-stride loops were slower.
+// ceiling of that pattern, the forward with a linear beta too (its up branch's
+// arithmetic hidden by the other wavefronts on the SIMD); the backward with a
+// linear beta needs two chunks per wavefront (the second one's loads in
+// flight during the first one's math) and four wavefronts per workgroup.
+// Longer chunk runs per wavefront and persistent grid-stride loops were
+// slower.
 // SITU_GLU_CHUNKS_PER_WAVE (1..8) and SITU_GLU_WAVES_PER_BLOCK (1..4) override
 // the choice (tuning).
 constexpr int kDrWavesPerBlock = 4;  // row mapping: target wavefronts per workgroup
@@ -346,7 +348,7 @@ int plan_split(int64_t rows, int64_t inter, int64_t es, bool bwd, bool lb, bool 
         g.magic = (uint32_t)((((uint64_t)1) << (31 + l)) / (uint64_t)cpr + 1);
         g.shift = l - 1;
     }
-    int k = es == 2 ? (group4 && cpr % 4 == 0 ? 4 : lb ? 2 : 1) : 2;
+    int k = es == 2 ? (group4 && cpr % 4 == 0 ? 4 : bwd && lb ? 2 : 1) : 2;
     int wpb = es == 2 && bwd && lb ? 4 : 1;
     if (env_k)
         k = env_k;
