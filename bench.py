@@ -415,6 +415,42 @@ def _cold_entry(ms, nbytes):
     return {"ms": round(ms, 5), "GB/s": round(gbs, 2), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
 
 
+def _graph_replay_ms(kernels: dict, nbytes: dict, n: int) -> dict:
+    """Launches too short for the host to keep the queue full (a few tens of
+    microseconds, against a few microseconds of Python and ctypes per call):
+    n back-to-back launches of each kernel recorded once in a HIP graph, the
+    graph replayed between two HIP events.  The kernels are the same; only
+    the host's launch cost leaves the measurement."""
+    import torch
+    out = {"launches_per_replay": n}
+    side = torch.cuda.Stream()
+    for name, fn in kernels.items():
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b) / n)
+        m = statistics.median(ms)
+        out[name] = {"ms": round(m, 5), "GB/s": round(nbytes[name] / (m / 1e3) / 1e9, 2),
+                     "pct_of_hbm_peak": round(100.0 * nbytes[name] / (m / 1e3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del g
+    return out
+
+
 def _cold_kernels(kernels: dict, nbytes: dict, n: int, dev) -> dict:
     """Cold-cache medians (a 512 MiB read before each launch) of the path's
     kernels alone: between HIP events on the launch stream, and kernel-only
@@ -799,6 +835,9 @@ def _elementwise(name: str, args, dev, full: bool) -> tuple:
             # every byte of such a launch fits in the Infinity Cache, so back-to-back
             # launches would read it from there: the cold medians are its number
             cold = _cold_kernels(ks, ab, min(args.steps, 20), dev)
+    graph = None
+    if not full and fwd_ms < 0.05:
+        graph = _graph_replay_ms({"fwd": fwd, "bwd": bwd} if w.backward else {"fwd": fwd}, ab, args.steps)
     ms_per_step = wall / args.steps * 1e3
     value = ab["total"] / (ms_per_step / 1e3) / 1e9
     dom = "bwd" if w.backward else "fwd"
@@ -833,6 +872,8 @@ def _elementwise(name: str, args, dev, full: bool) -> tuple:
                      "traffic": _traffic(name, dom, src)},
         "cold_cache_and_ceilings": cold,
     }
+    if graph is not None:
+        rec["kernels_graph_replay"] = graph
     return rec, x, outs
 
 
@@ -904,6 +945,8 @@ def main(argv=None) -> int:
                         "roofline_kernel": r["roofline"]["kernel"], "parity": par}
         if r["cold_cache_and_ceilings"] is not None:
             others[name]["cold"] = r["cold_cache_and_ceilings"]
+        if r.get("kernels_graph_replay") is not None:
+            others[name]["kernels_graph_replay"] = r["kernels_graph_replay"]
         if par is not None and not par["pass"]:
             others[name]["GB/s"] = None
         del xo, oo
